@@ -1,0 +1,429 @@
+"""Plain float64 CPU definition of the MoE layer, step by step -- test infrastructure only.
+
+Notation: T tokens, hidden D, E experts, top-k, expert hidden F. Pair id
+p = t*k + j for token t and slot j (slot 0 = best expert). Arrays are numpy;
+floating inputs are upcast exactly to float64 (bf16 and fp32 values are exact
+in float64).
+
+Readings taken where the pages are silent, ambiguous or garbled are marked
+READING and listed in the design notes.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "GATE_SOFTMAX_TOPK", "GATE_SIGMOID_TOPK", "GATE_SOFTMAX_FULL", "ACT_SWIGLU", "ACT_GELU",
+    "as_f64", "route_logits", "round_to_f32", "select_topk", "select_group_limited",
+    "group_scores", "gate_weights", "route", "decisive_tokens", "capacity", "dispatch_layout",
+    "send_counts", "dispatch_matrix", "permute", "silu", "gelu", "expert_ffn", "expert_ffn_rows",
+    "combine", "comm_volume_elements", "dispatch_volume_bytes", "layer_forward",
+]
+
+GATE_SOFTMAX_TOPK = 0
+GATE_SIGMOID_TOPK = 1
+GATE_SOFTMAX_FULL = 2
+ACT_SWIGLU = 0
+ACT_GELU = 1
+
+
+def as_f64(a) -> np.ndarray:
+    """Exact upcast of a float array (numpy, or a torch tensor of fp32/bf16) to float64."""
+    if hasattr(a, "detach"):  # torch tensor (bf16 has no numpy dtype): exact upcast on its side
+        a = a.detach().cpu().double().numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def round_to_f32(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest float32 (ties to even) and return them as float64."""
+    return np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Router: logits, selection, gates
+# ----------------------------------------------------------------------------------------------
+
+def route_logits(x, w_gate, bias=None) -> np.ndarray:
+    """Router logits l[t,e] = sum_d x[t,d] * W_g[e,d] + bias[e].
+
+    [EPLLM] section "The Execution Pipeline", step 1 (Router Gating): the
+    router scores each local token against all E experts with W_g x_t.
+    [EPLLM] "The Distributed MoE Dilemma": G(x) in R^E per token.
+    The optional per-expert bias is added to the logits (it moves both the
+    selection and the gate values; READING for the Switch-style workload).
+    """
+    x = as_f64(x)
+    wg = as_f64(w_gate)
+    l = x @ wg.T
+    if bias is not None:
+        l = l + as_f64(bias)[None, :]
+    return l
+
+
+def select_topk(l: np.ndarray, k: int, eligible: Optional[np.ndarray] = None) -> np.ndarray:
+    """Top-k expert indices per token, slot order = descending score.
+
+    [EPLLM] "The Execution Pipeline" step 1 and the layer equation of "The
+    Distributed MoE Dilemma" (sum over TopK(G(x), k)).
+    Ordering key is (-l[t,e], e): exact ties go to the lowest expert index.
+    Experts with ``eligible[t,e] == False`` are never chosen.
+    """
+    l = np.asarray(l, dtype=np.float64)
+    T, E = l.shape
+    key = l.copy()
+    if eligible is not None:
+        key = np.where(eligible, key, -np.inf)
+    # stable sort of -key keeps equal keys in ascending expert order
+    order = np.argsort(-key, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def group_scores(s: np.ndarray, n_groups: int, per_group_top: int) -> np.ndarray:
+    """Score of each expert group: the sum of its ``per_group_top`` largest member scores.
+
+    READING of node-limited routing ([EPA2A] "Three ways the system fights
+    back": a token may reach at most 4 nodes, chosen before per-expert
+    selection). Groups are contiguous blocks of E/n_groups experts, the same
+    contiguous map as expert -> device.
+    """
+    T, E = s.shape
+    g = s.reshape(T, n_groups, E // n_groups)
+    top = -np.sort(-g, axis=2)[:, :, :per_group_top]
+    return top.sum(axis=2)
+
+
+def select_group_limited(l: np.ndarray, k: int, n_groups: int, topk_groups: int,
+                         score: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Group-limited top-k: keep the best ``topk_groups`` groups, then top-k experts inside them.
+
+    Group ranking uses ``group_scores(score, ...)`` with k/topk_groups members
+    per group (READING), ordered by (-score_g, g); expert selection inside the
+    kept groups orders by (-l, e). Returns (topk_idx [T,k], kept_groups [T,topk_groups]).
+    """
+    T, E = l.shape
+    per_group_top = max(1, k // topk_groups)
+    gs = round_to_f32(group_scores(score, n_groups, per_group_top))
+    gorder = np.argsort(-gs, axis=1, kind="stable")[:, :topk_groups]
+    gsize = E // n_groups
+    eligible = np.zeros((T, E), dtype=bool)
+    for j in range(topk_groups):
+        g = gorder[:, j]
+        for m in range(gsize):
+            eligible[np.arange(T), g * gsize + m] = True
+    return select_topk(l, k, eligible), gorder
+
+
+def gate_weights(l: np.ndarray, topk_idx: np.ndarray, mode: int) -> np.ndarray:
+    """Gate values g[t,j] for the selected experts.
+
+    SOFTMAX_TOPK: g = Softmax(TopK(W_g x_t, k)) -- [EPLLM] "The Execution
+      Pipeline" step 1: softmax over the k selected logits only (renormalised).
+    SIGMOID_TOPK: g_j = sigmoid(l_j) / sum_i sigmoid(l_i) over the k selected
+      (READING for the DeepSeek-V3-shaped workload; the pages name DeepSeek-V3
+      routing in [EPA2A] without its gate formula).
+    SOFTMAX_FULL: g_j = softmax over all E logits, evaluated at the selected
+      experts (no renormalisation) -- the un-renormalised form of the layer
+      equation in [EPLLM] "The Distributed MoE Dilemma".
+    """
+    l = np.asarray(l, dtype=np.float64)
+    T = l.shape[0]
+    sel = np.take_along_axis(l, topk_idx, axis=1)
+    if mode == GATE_SOFTMAX_TOPK:
+        m = sel.max(axis=1, keepdims=True)
+        w = np.exp(sel - m)
+        return w / w.sum(axis=1, keepdims=True)
+    if mode == GATE_SIGMOID_TOPK:
+        s = 1.0 / (1.0 + np.exp(-sel))
+        return s / s.sum(axis=1, keepdims=True)
+    if mode == GATE_SOFTMAX_FULL:
+        m = l.max(axis=1, keepdims=True)
+        w = np.exp(l - m)
+        p = w / w.sum(axis=1, keepdims=True)
+        return np.take_along_axis(p, topk_idx, axis=1)
+    raise ValueError(f"unknown gate mode {mode}")
+
+
+def route(x, w_gate, bias, k: int, gate: int, n_groups: int = 0, topk_groups: int = 0) -> Dict[str, np.ndarray]:
+    """Router step end to end: logits, selection, gates.
+
+    Selection decisions are taken on the logits rounded to float32, the
+    precision the GPU kernel decides in; exact float32 ties go to the lowest
+    expert index. Gate values use the float64 logits.
+    """
+    l64 = route_logits(x, w_gate, bias)
+    l32 = round_to_f32(l64)
+    kept_groups = None
+    if n_groups and n_groups > 0:
+        s = 1.0 / (1.0 + np.exp(-l32)) if gate == GATE_SIGMOID_TOPK else l32
+        idx, kept_groups = select_group_limited(l32, k, n_groups, topk_groups, s)
+    else:
+        idx = select_topk(l32, k)
+    g = gate_weights(l64, idx, gate)
+    out = {"logits": l64, "topk_idx": idx, "topk_gate": g}
+    if kept_groups is not None:
+        out["kept_groups"] = kept_groups
+    return out
+
+
+def decisive_tokens(l: np.ndarray, k: int, margin: float = 1e-3, n_groups: int = 0,
+                    topk_groups: int = 0, gate: int = GATE_SOFTMAX_TOPK) -> Dict[str, np.ndarray]:
+    """Tokens whose selection cannot flip under float32 rounding of the logits.
+
+    ``set``: the k-th vs (k+1)-th logit margin among eligible experts exceeds
+    ``margin`` (and, with a group limit, the last kept vs first dropped group
+    score margin exceeds it too). ``order``: additionally every adjacent
+    margin among the top k exceeds ``margin``, so slot order is unique.
+    """
+    l = np.asarray(l, dtype=np.float64)
+    T, E = l.shape
+    ok_set = np.ones(T, dtype=bool)
+    eligible = None
+    if n_groups and n_groups > 0:
+        s = 1.0 / (1.0 + np.exp(-l)) if gate == GATE_SIGMOID_TOPK else l
+        gs = group_scores(s, n_groups, max(1, k // topk_groups))
+        gsorted = -np.sort(-gs, axis=1)
+        if topk_groups < n_groups:
+            ok_set &= (gsorted[:, topk_groups - 1] - gsorted[:, topk_groups]) > margin
+        gorder = np.argsort(-gs, axis=1, kind="stable")[:, :topk_groups]
+        gsize = E // n_groups
+        eligible = np.zeros((T, E), dtype=bool)
+        for j in range(topk_groups):
+            for m in range(gsize):
+                eligible[np.arange(T), gorder[:, j] * gsize + m] = True
+    key = l if eligible is None else np.where(eligible, l, -np.inf)
+    srt = -np.sort(-key, axis=1)
+    if k < E:
+        nxt = srt[:, k]
+        ok_set &= ~np.isfinite(nxt) | ((srt[:, k - 1] - nxt) > margin)
+    ok_order = ok_set.copy()
+    for j in range(k - 1):
+        ok_order &= (srt[:, j] - srt[:, j + 1]) > margin
+    return {"set": ok_set, "order": ok_order}
+
+
+# ----------------------------------------------------------------------------------------------
+# Dispatch layout: counts, capacity, stable grouping by expert, per-rank send layout
+# ----------------------------------------------------------------------------------------------
+
+def capacity(capacity_factor: float, T: int, k: int, E: int) -> int:
+    """Expert capacity C = ceil(CF * k * T / E), T = B*S.
+
+    [EPLLM] "Static Capacity Factors and Token Dropping", capacity equation.
+    Evaluated once in IEEE double exactly as written. CF <= 0 means dropless:
+    C = T*k (no expert can receive more pairs than exist).
+    """
+    if capacity_factor is None or capacity_factor <= 0:
+        return T * k
+    return int(math.ceil(capacity_factor * (k * T) / E))
+
+
+def dispatch_layout(topk_idx: np.ndarray, E: int, ep_size: int, C: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Group (token, expert) pairs into contiguous per-expert rows; per-rank send counts.
+
+    [EPA2A] "The two exchanges" (dispatch: each device sorts its tokens by
+    destination expert into groups); [EPLLM] "The Execution Pipeline" step 1
+    (each token is replicated k times, tagged with expert and destination
+    rank) and step 2 (local permutation into contiguous per-rank buffers);
+    [A2AC] the dispatch example (destination device = expert //
+    experts_per_device; send counts = per-device bincount).
+
+    READINGS: rows are ordered by (expert ascending, pair id ascending) --
+    stable, which the example's unstable device-only sort is not. With a
+    capacity C ([EPLLM] "Static Capacity Factors"), each expert keeps its
+    first C pairs in pair-id (token) order and drops the rest; dropped pairs
+    get row -1. The layout is compact (no padding slots).
+    """
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    T, k = idx.shape
+    P = T * k
+    flat = idx.reshape(-1)                          # pair id p = t*k + j
+    if C is None:
+        C = P
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable")         # pairs by (expert, pair id)
+    first = np.concatenate([[0], np.cumsum(counts)])[:E]
+    rank_in_expert = np.empty(P, dtype=np.int64)
+    rank_in_expert[order] = np.arange(P) - first[flat[order]]
+    kept = rank_in_expert < C
+    kept_counts = np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept_counts)]).astype(np.int64)
+    N = int(offsets[E])
+    pair_to_row = np.where(kept, offsets[flat] + rank_in_expert, -1).astype(np.int64)
+    row_to_pair = np.full(P, -1, dtype=np.int64)
+    row_to_pair[pair_to_row[kept]] = np.arange(P)[kept]
+    epr = E // ep_size                              # experts per rank, contiguous blocks
+    rank_counts = kept_counts.reshape(ep_size, epr).sum(axis=1)
+    rank_offsets = offsets[::epr].copy()            # o_{r*E/EP}, r = 0..EP
+    return {
+        "expert_counts": counts, "kept_counts": kept_counts, "expert_offsets": offsets,
+        "rank_counts": rank_counts, "rank_offsets": rank_offsets,
+        "pair_to_row": pair_to_row, "row_to_pair": row_to_pair, "n_kept": N, "capacity": C,
+        "n_dropped": P - N,
+    }
+
+
+def send_counts(topk_idx: np.ndarray, E: int, world_size: int) -> np.ndarray:
+    """Pairs bound for each device: bincount(expert // (E / world_size)).
+
+    [A2AC] the dispatch example (destination = expert // experts_per_device,
+    send counts by bincount with one bin per device).
+    """
+    dest = np.asarray(topk_idx, dtype=np.int64).reshape(-1) // (E // world_size)
+    return np.bincount(dest, minlength=world_size)
+
+
+def dispatch_matrix(topk_idx_per_src: np.ndarray, E: int, n_dev: int) -> np.ndarray:
+    """[src, dst] counts of (token, expert) pairs for n_dev source shards.
+
+    [A2AC] the routing simulation: each source device's pairs are counted by
+    destination device = expert // (E / n_dev).
+    """
+    out = np.zeros((n_dev, n_dev), dtype=np.int64)
+    for src in range(n_dev):
+        out[src] = send_counts(topk_idx_per_src[src], E, n_dev)
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Permute, expert FFN, combine
+# ----------------------------------------------------------------------------------------------
+
+def permute(x, row_to_pair: np.ndarray, k: int, n_rows: Optional[int] = None) -> np.ndarray:
+    """x_perm[r] = x[row_to_pair[r] // k] for the kept rows r < N.
+
+    [EPLLM] "The Execution Pipeline" step 2 (tokens are physically reordered
+    into contiguous buffers). Values are copied unchanged.
+    """
+    r2p = np.asarray(row_to_pair, dtype=np.int64)
+    if n_rows is None:
+        n_rows = int((r2p >= 0).sum())
+    xa = np.asarray(x) if not hasattr(x, "detach") else as_f64(x)
+    return xa[r2p[:n_rows] // k]
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """SiLU(a) = a * sigmoid(a)."""
+    return a / (1.0 + np.exp(-a))
+
+
+def gelu(a: np.ndarray) -> np.ndarray:
+    """Exact GELU: a * Phi(a) = a/2 * (1 + erf(a / sqrt 2)) (READING: the erf form)."""
+    return 0.5 * a * (1.0 + _erf(a / math.sqrt(2.0)))
+
+
+def _expert_rows(rows: np.ndarray, w1, w3, w2, act: int) -> np.ndarray:
+    a = rows @ as_f64(w1).T                    # [n, F]
+    if act == ACT_SWIGLU:
+        b = rows @ as_f64(w3).T                # [n, F]
+        h = silu(a) * b                        # SiLU(W1 x) * (W3 x)
+    elif act == ACT_GELU:
+        h = gelu(a)
+    else:
+        raise ValueError(f"unknown activation {act}")
+    return h @ as_f64(w2).T                    # [n, D]
+
+
+def expert_ffn(x_perm, expert_offsets: np.ndarray, w1, w3, w2, act: int) -> np.ndarray:
+    """Per-expert FFN over each expert's contiguous rows.
+
+    [EPLLM] "The Execution Pipeline" step 4: all rows bound for one local
+    expert go through one batched GEMM; the expert is
+    W2 * (SiLU(W1 h) (*) (W3 h)) -- READING of the garbled parenthesisation as
+    SwiGLU, SiLU applied to W1 h alone. GELU experts use two matrices:
+    W2 * GELU(W1 h) ([COMM]: two matrix multiplications per token).
+    Weights: W1, W3 [E,F,D]; W2 [E,D,F].
+    """
+    xp = as_f64(x_perm)
+    off = np.asarray(expert_offsets, dtype=np.int64)
+    E = off.shape[0] - 1
+    out = np.zeros((int(off[E]), xp.shape[1] if xp.ndim == 2 else 0), dtype=np.float64)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi <= lo:
+            continue
+        out[lo:hi] = _expert_rows(xp[lo:hi], w1[e], None if w3 is None else w3[e], w2[e], act)
+    return out
+
+
+def expert_ffn_rows(rows, experts: np.ndarray, w1, w3, w2, act: int) -> np.ndarray:
+    """The same expert FFN for an arbitrary set of rows, row i going through expert experts[i].
+
+    Used to check sampled rows at full size; ``w1`` etc. may be callables
+    ``e -> matrix`` so one expert's weights are fetched at a time.
+    """
+    xr = as_f64(rows)
+    ex = np.asarray(experts, dtype=np.int64)
+    D = xr.shape[1]
+    out = np.zeros((xr.shape[0], D), dtype=np.float64)
+    get = (lambda w, e: None if w is None else (w(e) if callable(w) else w[e]))
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        out[sel] = _expert_rows(xr[sel], get(w1, e), get(w3, e), get(w2, e), act)
+    return out
+
+
+def combine(y_perm, pair_to_row: np.ndarray, topk_gate, T: int, k: int) -> np.ndarray:
+    """y[t] = sum over kept slots j of g[t,j] * y_perm[pair_to_row[t*k + j]].
+
+    [EPLLM] "The Execution Pipeline" step 6 (restore order, scale each of the
+    k outputs by its gate and sum them; the residual is added outside) and the
+    layer equation of "The Distributed MoE Dilemma". A dropped pair adds
+    nothing, so a token with every pair dropped comes out as exactly 0
+    (READING; gates are not renormalised after drops).
+    """
+    yp = as_f64(y_perm)
+    g = as_f64(topk_gate).reshape(T, k)
+    p2r = np.asarray(pair_to_row, dtype=np.int64).reshape(T, k)
+    D = yp.shape[1]
+    y = np.zeros((T, D), dtype=np.float64)
+    for j in range(k):
+        rows = p2r[:, j]
+        kept = rows >= 0
+        y[kept] += g[kept, j][:, None] * yp[rows[kept]]
+    return y
+
+
+# ----------------------------------------------------------------------------------------------
+# Volume accounting
+# ----------------------------------------------------------------------------------------------
+
+def comm_volume_elements(n_kept: int, D: int) -> int:
+    """Elements moved by dispatch + combine: 2 * (kept pairs) * D.
+
+    [COMM] the per-layer volume equation V = 2*B*S*K*D; with capacity drops
+    the kept-pair count replaces B*S*K (READING).
+    """
+    return 2 * int(n_kept) * int(D)
+
+
+def dispatch_volume_bytes(n_remote: int, D: int, elem_bytes: int) -> int:
+    """Bytes one device sends in dispatch: its remote pairs * D * sizeof(dtype).
+
+    [EPLLM] "Communication Volume and Hardware Topology", the per-GPU dispatch
+    volume equation (B*S*k*H*(EP-1)/EP*sizeof under uniform routing; here the
+    exact remote-pair count replaces its expectation).
+    """
+    return int(n_remote) * int(D) * int(elem_bytes)
+
+
+# ----------------------------------------------------------------------------------------------
+# The whole layer
+# ----------------------------------------------------------------------------------------------
+
+def layer_forward(inputs: Dict, cfg) -> Dict[str, np.ndarray]:
+    """Router -> layout -> permute -> expert FFN -> combine on one device, all in float64."""
+    r = route(inputs["x"], inputs["w_gate"], inputs.get("bias"), cfg.top_k, cfg.gate,
+              cfg.n_groups, cfg.topk_groups)
+    C = capacity(cfg.capacity_factor, cfg.T, cfg.top_k, cfg.E)
+    lay = dispatch_layout(r["topk_idx"], cfg.E, cfg.ep_size, C)
+    xp = permute(as_f64(inputs["x"]), lay["row_to_pair"], cfg.top_k, lay["n_kept"])
+    yp = expert_ffn(xp, lay["expert_offsets"], inputs["w1"], inputs.get("w3"), inputs["w2"], cfg.act)
+    y = combine(yp, lay["pair_to_row"], r["topk_gate"], cfg.T, cfg.top_k)
+    out = dict(r)
+    out.update(lay)
+    out.update({"x_perm": xp, "y_perm": yp, "y": y})
+    return out
