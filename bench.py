@@ -1,0 +1,213 @@
+"""Throughput of the one-GPU MoE layer (route -> layout -> permute -> expert FFN -> combine).
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
+
+One step = one full layer forward over one batch of seeded synthetic input already resident in
+HBM: all five stages, enqueued back to back on one stream with no host synchronisation. Prints
+ONE JSON line on stdout; diagnostics go to stderr.
+
+value = T / (ms_per_step / 1e3) tokens/s on the one GPU. The roofline object is for the dominant
+kernel (the grouped up-projection GEMM with the fused SwiGLU/GELU epilogue), timed with HIP
+events around its launch on the stream it runs on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s (route+permute+FFN+combine); permute GB/s; GEMM MFMA %"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+STAGES = ["route", "layout", "permute", "ffn_up", "ffn_down", "combine"]
+DOMINANT = "ffn_up"
+DOMINANT_SRC = os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip")
+CPU_SAMPLE_TOKENS = {"tiny_fp32": 256, "switch_cap": 2048, "mixtral": 64, "dsv3": 40, "skew": 256}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC summary, or None
+    if there is none or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_ffn_up_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_sha(DOMINANT_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(cfg, inp, n_tokens: int):
+    """The CPU oracle, untouched, on the first n_tokens tokens of the same workload."""
+    import numpy as np
+    import threadpoolctl
+    import oracle as O
+
+    S = min(n_tokens, cfg.T)
+    x = inp["x"][:S].cpu()
+    wg = inp["w_gate"].cpu()
+    bias = None if inp["bias"] is None else inp["bias"].cpu()
+    # which experts the sample reaches (so their weights are in host memory before timing)
+    r0 = O.route(x, wg, bias, cfg.top_k, cfg.gate, cfg.n_groups, cfg.topk_groups)
+    experts = sorted(set(np.asarray(r0["topk_idx"]).reshape(-1).tolist()))
+    host_w = {key: ({e: inp[key][e].cpu() for e in experts} if inp[key] is not None else None)
+              for key in ("w1", "w3", "w2")}
+    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) if threadpoolctl.threadpool_info() else 1
+    t0 = time.perf_counter()
+    r = O.route(x, wg, bias, cfg.top_k, cfg.gate, cfg.n_groups, cfg.topk_groups)
+    C = O.capacity(cfg.capacity_factor, S, cfg.top_k, cfg.E)
+    lay = O.dispatch_layout(r["topk_idx"], cfg.E, cfg.ep_size, C)
+    xp = O.permute(O.as_f64(x), lay["row_to_pair"], cfg.top_k, lay["n_kept"])
+    yp = O.expert_ffn(xp, lay["expert_offsets"], host_w["w1"], host_w["w3"], host_w["w2"], cfg.act)
+    O.combine(yp, lay["pair_to_row"], r["topk_gate"], S, cfg.top_k)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {S} of {cfg.T} tokens ({S * cfg.top_k} pairs, {len(experts)} experts' weights "
+                      f"in host memory), whole layer in float64, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures the one-GPU share of the MoE layer only: run it with --gpus 1 "
+              "(multi-GPU expert parallelism is not part of this build).", file=sys.stderr)
+        return 2
+
+    import torch
+    import combine_experts_amd as M
+    import workloads as W
+
+    M.load_library()
+    cfg = W.get_config(args.workload)
+    dev = "cuda"
+    log(f"[bench] {cfg.desc}")
+    t0 = time.time()
+    inp = W.make_inputs(cfg, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs drawn on GPU in {time.time() - t0:.1f} s")
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, None, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
+                              buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        M.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], buf.h, stream)
+        if ev is not None:
+            ev[4].record(stream)
+        M.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm, stream)
+        if ev is not None:
+            ev[5].record(stream)
+        M.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
+        if ev is not None:
+            ev[6].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, s in enumerate(STAGES)}
+
+    N = int(buf.expert_offsets[-1].item())
+    counts = buf.expert_counts.cpu()
+    b = 2 if cfg.dtype == W.DT_BF16 else 4
+    nm = 3 if cfg.act == W.ACT_SWIGLU else 2
+    up_flops = 2.0 * N * cfg.D * cfg.F * (nm - 1)
+    ffn_flops = 2.0 * N * cfg.D * cfg.F * nm
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == W.DT_BF16 else PEAK_F32_TFLOPS
+    up_tflops = up_flops / (stage_ms[DOMINANT] * 1e-3) / 1e12
+    ffn_tflops = ffn_flops / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e-3) / 1e12
+    permute_bytes = cfg.T * cfg.D * b + N * cfg.D * b + cfg.T * cfg.top_k * 4
+    combine_bytes = N * cfg.D * b + cfg.T * cfg.D * b + cfg.T * cfg.top_k * 8
+    permute_gbs = permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9
+    combine_gbs = combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9
+    traffic = read_traffic(cfg.name)
+    roofline = {"bound": "mfma", "achieved": round(up_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(up_tflops / peak, 4), "traffic": traffic,
+                "kernel": "ffn_gemm_bf16 (grouped up-projection, fused SwiGLU)" if cfg.dtype == W.DT_BF16
+                else "ffn_gemm_f32 (grouped up-projection)",
+                "algorithmic_flops_per_launch": up_flops}
+    log(f"[bench] N={N} kept rows, max/mean expert count {float(counts.max()) / float(counts.float().mean()):.2f}")
+    for s in STAGES:
+        log(f"[bench]   {s:9s} {stage_ms[s] * 1e3:9.1f} us")
+    log(f"[bench] permute {permute_gbs:.0f} GB/s, combine {combine_gbs:.0f} GB/s, "
+        f"FFN {ffn_tflops:.0f} TFLOP/s ({ffn_tflops / peak * 100:.1f}% of peak)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(cfg.name, 8)
+        log(f"[bench] CPU oracle baseline on {n} tokens ...")
+        cpu = cpu_baseline(cfg, inp, n)
+        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(cfg.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == W.DT_BF16 else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "top_k": cfg.top_k, "F": cfg.F,
+                   "act": "swiglu" if cfg.act == W.ACT_SWIGLU else "gelu", "capacity_factor": cfg.capacity_factor,
+                   "ep_size_emulated": cfg.ep_size, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
+                   "kept_rows": N, "parallelism": "1 GPU"},
+        "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
+        "gemm_mfma_frac": round(ffn_tflops / peak, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Every function here has the name of the C entry point it calls (see include/moe.h), takes torch
+tensors for the device buffers, checks their device, dtype, shape and contiguity, passes raw
+pointers plus the current HIP stream, and raises ``MoEError`` on a non-zero status. All work of
+the layer runs in the library's HIP kernels; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
+MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL = 0, 1, 2
+MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
+MOE_F32, MOE_BF16 = 0, 1
+MOE_STAGE_LAYOUT, MOE_STAGE_FFN = 0, 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "D", "E", "top_k", "F", "ep_size", "ep_rank", "n_groups", "topk_groups",
+                 "gate", "act", "dtype")] + [("capacity_factor", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_SIG = {
+    "moe_abi_version": (ctypes.c_int, []),
+    "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_capacity": (ctypes.c_int, [ctypes.POINTER(moe_dims), _I32P]),
+    "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
+    "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
+    "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "moe_expert_ffn_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_down": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by ``combine_experts_amd.build``). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmoe.so not found at {path}: build it with `python -m combine_experts_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIG.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        msg = load_library().moe_status_str(status).decode()
+        raise MoEError(fn, status, msg)
+
+
+def make_dims(T, D, E, top_k, F, *, ep_size=1, ep_rank=0, n_groups=0, topk_groups=0,
+              gate=MOE_GATE_SOFTMAX_TOPK, act=MOE_ACT_SWIGLU, dtype=MOE_BF16, capacity_factor=0.0) -> moe_dims:
+    return moe_dims(T, D, E, top_k, F, ep_size, ep_rank, n_groups, topk_groups, gate, act, dtype,
+                    float(capacity_factor))
+
+
+def dims_from_config(cfg) -> moe_dims:
+    """moe_dims of a workloads.MoEConfig (or anything with the same attribute names)."""
+    return make_dims(cfg.T, cfg.D, cfg.E, cfg.top_k, cfg.F, ep_size=cfg.ep_size, ep_rank=cfg.ep_rank,
+                     n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, gate=cfg.gate, act=cfg.act,
+                     dtype=cfg.dtype, capacity_factor=cfg.capacity_factor)
+
+
+def _elem_dtype(d: moe_dims) -> torch.dtype:
+    return torch.bfloat16 if d.dtype == MOE_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor], name: str, dtype=None, numel=None, nullable=False) -> Optional[int]:
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} needs at least {numel} elements, has {t.numel()}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ----------------------------------------------------------------------------------------------
+# Entry points (same names as the C ABI)
+# ----------------------------------------------------------------------------------------------
+
+def moe_abi_version() -> int:
+    return load_library().moe_abi_version()
+
+
+def moe_status_str(status: int) -> str:
+    return load_library().moe_status_str(status).decode()
+
+
+def moe_capacity(d: moe_dims) -> int:
+    c = ctypes.c_int32(0)
+    _check("moe_capacity", load_library().moe_capacity(ctypes.byref(d), ctypes.byref(c)))
+    return c.value
+
+
+def moe_workspace_size(d: moe_dims, stage: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("moe_workspace_size", load_library().moe_workspace_size(ctypes.byref(d), stage, ctypes.byref(b)))
+    return b.value
+
+
+def moe_route(d: moe_dims, x, w_gate, bias, topk_idx, topk_gate, logits=None, stream=None) -> None:
+    dt = _elem_dtype(d)
+    st = load_library().moe_route(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D), _ptr(w_gate, "w_gate", dt, d.E * d.D),
+        _ptr(bias, "bias", torch.float32, d.E, nullable=True),
+        _ptr(topk_idx, "topk_idx", torch.int32, d.T * d.top_k), _ptr(topk_gate, "topk_gate", torch.float32, d.T * d.top_k),
+        _ptr(logits, "logits", torch.float32, d.T * d.E, nullable=True), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_dispatch_layout(d: moe_dims, topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                        pair_to_row, row_to_pair, ws, stream=None) -> None:
+    P = d.T * d.top_k
+    i32 = torch.int32
+    st = load_library().moe_dispatch_layout(
+        ctypes.byref(d), _ptr(topk_idx, "topk_idx", i32, P), _ptr(expert_counts, "expert_counts", i32, d.E),
+        _ptr(expert_offsets, "expert_offsets", i32, d.E + 1), _ptr(rank_counts, "rank_counts", i32, d.ep_size),
+        _ptr(rank_offsets, "rank_offsets", i32, d.ep_size + 1), _ptr(pair_to_row, "pair_to_row", i32, P),
+        _ptr(row_to_pair, "row_to_pair", i32, P), _ptr(ws, "ws", nullable=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_dispatch_layout", st)
+
+
+def moe_permute(d: moe_dims, x, pair_to_row, x_perm, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_permute(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        _ptr(x_perm, "x_perm", dt, P * d.D), _stream(stream))
+    _check("moe_permute", st)
+
+
+def moe_expert_ffn_up(d: moe_dims, x_perm, expert_offsets, w1, w3, h, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up(
+        ctypes.byref(d), _ptr(x_perm, "x_perm", dt, P * d.D), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(h, "h", dt, P * d.F), _stream(stream))
+    _check("moe_expert_ffn_up", st)
+
+
+def moe_expert_ffn_down(d: moe_dims, h, expert_offsets, w2, y_perm, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_down(
+        ctypes.byref(d), _ptr(h, "h", dt, P * d.F), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_perm, "y_perm", dt, P * d.D), _stream(stream))
+    _check("moe_expert_ffn_down", st)
+
+
+def moe_expert_ffn(d: moe_dims, x_perm, expert_offsets, w1, w3, w2, y_perm, ws, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn(
+        ctypes.byref(d), _ptr(x_perm, "x_perm", dt, P * d.D), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_perm, "y_perm", dt, P * d.D), _ptr(ws, "ws", nullable=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_expert_ffn", st)
+
+
+def moe_unpermute_combine(d: moe_dims, y_perm, pair_to_row, topk_gate, y, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_unpermute_combine(
+        ctypes.byref(d), _ptr(y_perm, "y_perm", dt, P * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        _ptr(topk_gate, "topk_gate", torch.float32, P), _ptr(y, "y", dt, d.T * d.D), _stream(stream))
+    _check("moe_unpermute_combine", st)

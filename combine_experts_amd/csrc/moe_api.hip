@@ -1,0 +1,187 @@
+// libmoe C ABI: host-side argument checks and kernel launches. Nothing here allocates, frees or
+// synchronises; every call enqueues work on the caller's stream and returns a status.
+#include <cmath>
+#include <cstdint>
+
+#include "moe_common.h"
+
+namespace {
+
+constexpr int kAbiVersion = 100;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+int elem_bytes(const moe_dims* d) { return d->dtype == MOE_BF16 ? 2 : 4; }
+
+// Consistency of the problem statement itself (shared by every entry point).
+int check_dims(const moe_dims* d) {
+  if (d == nullptr) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->D <= 0 || d->E <= 0 || d->F <= 0) return MOE_ERR_INVALID_ARG;
+  if (d->top_k < 1 || d->top_k > d->E) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)d->T * d->top_k > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (d->ep_size < 1 || d->E % d->ep_size != 0) return MOE_ERR_INVALID_ARG;
+  if (d->ep_rank < 0 || d->ep_rank >= d->ep_size) return MOE_ERR_INVALID_ARG;
+  if (d->n_groups < 0) return MOE_ERR_INVALID_ARG;
+  if (d->n_groups > 0) {
+    if (d->E % d->n_groups != 0) return MOE_ERR_INVALID_ARG;
+    if (d->topk_groups < 1 || d->topk_groups > d->n_groups) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)d->topk_groups * (d->E / d->n_groups) < d->top_k) return MOE_ERR_INVALID_ARG;
+  }
+  if (d->gate < MOE_GATE_SOFTMAX_TOPK || d->gate > MOE_GATE_SOFTMAX_FULL) return MOE_ERR_INVALID_ARG;
+  if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_GELU) return MOE_ERR_INVALID_ARG;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(d->capacity_factor)) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int32_t capacity_of(const moe_dims* d) {
+  const int64_t n_pairs = (int64_t)d->T * d->top_k;
+  if (d->capacity_factor <= 0.0) return (int32_t)n_pairs;
+  // C = ceil(CF * k * T / E), in IEEE double, evaluated as CF * (k*T) / E
+  const double c = std::ceil(d->capacity_factor * (double)n_pairs / (double)d->E);
+  if (c >= (double)n_pairs) return (int32_t)n_pairs;
+  return (int32_t)c;
+}
+
+size_t ffn_ws_bytes(const moe_dims* d) {
+  const size_t n_max = (size_t)d->T * d->top_k;
+  return (n_max * d->F * elem_bytes(d) + 255) / 256 * 256;
+}
+
+int row_vec_ok(const moe_dims* d, int n) { return (n * elem_bytes(d)) % 16 == 0; }
+
+int ffn_shape_ok(const moe_dims* d) {
+  if (d->dtype == MOE_BF16) return d->D % 64 == 0 && d->F % 64 == 0;
+  return d->D % 16 == 0 && d->F % 16 == 0;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, inconsistent dims or misaligned pointer";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid dims with no kernel in this build";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_capacity(const moe_dims* d, int32_t* capacity) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (capacity == nullptr) return MOE_ERR_INVALID_ARG;
+  *capacity = capacity_of(d);
+  return MOE_OK;
+}
+
+int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (stage == MOE_STAGE_LAYOUT) {
+    *bytes = moe::layout_ws_bytes(d->T * d->top_k, d->E);
+  } else if (stage == MOE_STAGE_FFN) {
+    *bytes = ffn_ws_bytes(d);
+  } else {
+    return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias, int32_t* topk_idx,
+              float* topk_gate, float* logits, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;  // nothing to route
+  if (x == nullptr || w_gate == nullptr || topk_idx == nullptr || topk_gate == nullptr) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned4(topk_idx) || !aligned4(topk_gate)) return MOE_ERR_INVALID_ARG;
+  if ((bias && !aligned4(bias)) || (logits && !aligned4(logits))) return MOE_ERR_INVALID_ARG;
+  if (d->E > 256 || d->top_k > 32 || d->D % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->n_groups > 64 || (d->n_groups > 0 && d->top_k / d->topk_groups > 8)) return MOE_ERR_UNSUPPORTED;
+  moe::RouteArgs a{x, w_gate, bias, topk_idx, topk_gate, logits, d->T, d->D, d->E, d->top_k,
+                   d->n_groups, d->n_groups > 0 ? d->topk_groups : 0, d->gate};
+  return hip_status(moe::launch_route(a, d->dtype, stream));
+}
+
+int moe_dispatch_layout(const moe_dims* d, const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,
+                        int32_t* rank_counts, int32_t* rank_offsets, int32_t* pair_to_row, int32_t* row_to_pair,
+                        void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!topk_idx || !pair_to_row || !row_to_pair)) return MOE_ERR_INVALID_ARG;
+  if (d->E > 1024) return MOE_ERR_UNSUPPORTED;
+  const int32_t n_pairs = d->T * d->top_k;
+  if (ws == nullptr || ws_bytes < moe::layout_ws_bytes(n_pairs, d->E)) return MOE_ERR_WORKSPACE;
+  if (!aligned4(ws)) return MOE_ERR_INVALID_ARG;
+  moe::LayoutArgs a{topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets, pair_to_row, row_to_pair,
+                    static_cast<int32_t*>(ws), n_pairs, d->E, d->ep_size, capacity_of(d)};
+  return hip_status(moe::launch_layout(a, stream));
+}
+
+int moe_permute(const moe_dims* d, const void* x, const int32_t* pair_to_row, void* x_perm, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !pair_to_row || !x_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_permute(x, pair_to_row, x_perm, d->T, d->D, d->top_k, d->dtype, stream));
+}
+
+int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                      const void* w3, void* h, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w1 || !h || (d->act == MOE_ACT_SWIGLU && !w3)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(h) || (w3 && !aligned16(w3))) return MOE_ERR_INVALID_ARG;
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a{x_perm, expert_offsets, w1, d->act == MOE_ACT_SWIGLU ? w3 : nullptr, h,
+                 d->T * d->top_k, d->E, d->D, d->F, d->act};
+  return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(a, stream) : moe::launch_ffn_f32(a, stream));
+}
+
+int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_offsets, const void* w2,
+                        void* y_perm, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!h || !expert_offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(y_perm)) return MOE_ERR_INVALID_ARG;
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a{h, expert_offsets, w2, nullptr, y_perm, d->T * d->top_k, d->E, d->F, d->D, -1};
+  return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(a, stream) : moe::launch_ffn_f32(a, stream));
+}
+
+int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                   const void* w3, const void* w2, void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (ws == nullptr || ws_bytes < ffn_ws_bytes(d)) return MOE_ERR_WORKSPACE;
+  st = moe_expert_ffn_up(d, x_perm, expert_offsets, w1, w3, ws, stream);
+  if (st != MOE_OK) return st;
+  return moe_expert_ffn_down(d, ws, expert_offsets, w2, y_perm, stream);
+}
+
+int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row, const float* topk_gate,
+                          void* y, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!y_perm || !pair_to_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_combine(y_perm, pair_to_row, topk_gate, y, d->T, d->D, d->top_k, d->dtype, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,82 @@
+// Internal declarations shared by libmoe's translation units (device helpers + launch wrappers).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe.h"
+
+#define MOE_WAVE 64
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// float -> bf16, round to nearest even (the C conversion; gfx950 has a native instruction for it)
+__device__ __forceinline__ bf16_t f2bf(float f) { return static_cast<bf16_t>(f); }
+__device__ __forceinline__ float bf2f(bf16_t b) { return static_cast<float>(b); }
+
+// Element conversions used by the templated kernels.
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ------------------------------------------------------------------------------------------------
+// Launch wrappers, one per translation unit (host-callable; all return hipError_t of the launch).
+// ------------------------------------------------------------------------------------------------
+namespace moe {
+
+struct LayoutArgs {
+  const int32_t* topk_idx;
+  int32_t* expert_counts;
+  int32_t* expert_offsets;
+  int32_t* rank_counts;
+  int32_t* rank_offsets;
+  int32_t* pair_to_row;
+  int32_t* row_to_pair;
+  int32_t* chunk_hist;  // workspace: [n_chunks, E]
+  int32_t n_pairs, E, ep_size, capacity;
+};
+constexpr int kLayoutChunk = 512;  // pairs per wave-sized chunk of the stable layout
+size_t layout_ws_bytes(int32_t n_pairs, int32_t E);
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+
+struct RouteArgs {
+  const void* x;
+  const void* w_gate;
+  const float* bias;
+  int32_t* topk_idx;
+  float* topk_gate;
+  float* logits;
+  int32_t T, D, E, k, n_groups, topk_groups, gate;
+};
+hipError_t launch_route(const RouteArgs& a, int dtype, hipStream_t s);
+
+hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_perm, int32_t T, int32_t D,
+                          int32_t k, int dtype, hipStream_t s);
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, void* y,
+                          int32_t T, int32_t D, int32_t k, int dtype, hipStream_t s);
+
+struct FfnArgs {
+  const void* a;              // x_perm (up) or h (down): [N_max, K]
+  const int32_t* expert_offsets;
+  const void* b0;             // W1 (up) or W2 (down): [E, Nout, K]
+  const void* b1;             // W3 (up, SwiGLU) or null
+  void* out;                  // h (up) or y_perm (down): [N_max, Nout]
+  int32_t n_rows_max, E, K, Nout;
+  int act;                    // up: MOE_ACT_*; down: -1 (no activation)
+};
+hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
+
+}  // namespace moe

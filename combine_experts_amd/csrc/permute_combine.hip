@@ -1,0 +1,131 @@
+// Permute (dispatch side) and unpermute + combine (combine side) of the one-GPU MoE layer.
+//
+// EP-in-LLMs article, "The Execution Pipeline": step 2 reorders each token's k copies into
+// contiguous per-expert / per-rank buffers; step 6 restores token order, scales each of the k
+// expert outputs by its gate and sums them. On one GPU the send buffer of step 2 is also the
+// receive buffer of step 4, so the two all-to-alls of steps 3 and 5 move nothing.
+//
+// Both kernels are HBM-bound row copies: one wave per token, 16-byte accesses, several chunks in
+// flight per lane. Permute reads each x row once and writes it to its k rows; combine reads the k
+// rows of a token, sums gate * row in float32 in slot order and rounds once.
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kUnroll = 4;
+
+template <typename T>
+struct Vec;
+template <>
+struct Vec<bf16_t> {
+  static constexpr int N = 8;
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+};
+
+__global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ x, const int32_t* __restrict__ p2r,
+                                                      u32x4* __restrict__ xp, int T, int row_chunks, int k) {
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  for (int t = blockIdx.x * kWaves + wave; t < T; t += gridDim.x * kWaves) {
+    const u32x4* src = x + (size_t)t * row_chunks;
+    for (int c0 = 0; c0 < row_chunks; c0 += MOE_WAVE * kUnroll) {
+      u32x4 v[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        if (c < row_chunks) v[u] = __builtin_nontemporal_load(src + c);
+      }
+      for (int j = 0; j < k; ++j) {
+        const int row = p2r[(size_t)t * k + j];
+        if (row < 0) continue;
+        u32x4* dst = xp + (size_t)row * row_chunks;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          if (c < row_chunks) dst[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ p2r,
+                                                      const float* __restrict__ gate, T* __restrict__ y, int T_,
+                                                      int D, int k) {
+  constexpr int VN = Vec<T>::N;
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  const int row_chunks = D / VN;
+  for (int t = blockIdx.x * kWaves + wave; t < T_; t += gridDim.x * kWaves) {
+    for (int c0 = 0; c0 < row_chunks; c0 += MOE_WAVE * kUnroll) {
+      float acc[kUnroll][VN];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[u][i] = 0.f;
+      for (int j = 0; j < k; ++j) {
+        const int row = p2r[(size_t)t * k + j];
+        if (row < 0) continue;
+        const float g = gate[(size_t)t * k + j];
+        const T* src = yp + (size_t)row * D;
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          if (c < row_chunks) {
+            const u32x4 raw = *reinterpret_cast<const u32x4*>(src + (size_t)c * VN);
+            const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[u][i] = fmaf(g, to_f32<T>(e[i]), acc[u][i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        if (c < row_chunks) {
+          u32x4 raw;
+          T* e = reinterpret_cast<T*>(&raw);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) e[i] = from_f32<T>(acc[u][i]);
+          __builtin_nontemporal_store(raw, reinterpret_cast<u32x4*>(y + (size_t)t * D) + c);
+        }
+      }
+    }
+  }
+}
+
+int grid_for(int T) {
+  const int blocks = (T + kWaves - 1) / kWaves;
+  return blocks < 65535 * 4 ? blocks : 65535 * 4;
+}
+
+}  // namespace
+
+hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_perm, int32_t T, int32_t D, int32_t k,
+                          int dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int elem = dtype == MOE_BF16 ? 2 : 4;
+  const int row_chunks = D * elem / 16;
+  hipLaunchKernelGGL(permute_kernel, dim3(grid_for(T)), dim3(256), 0, s, (const u32x4*)x, pair_to_row,
+                     (u32x4*)x_perm, T, row_chunks, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, void* y, int32_t T,
+                          int32_t D, int32_t k, int dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (dtype == MOE_BF16) {
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid_for(T)), dim3(256), 0, s, (const bf16_t*)y_perm,
+                       pair_to_row, gate, (bf16_t*)y, T, D, k);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid_for(T)), dim3(256), 0, s, (const float*)y_perm,
+                       pair_to_row, gate, (float*)y, T, D, k);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,170 @@
+/*
+ * moe.h -- C ABI of libmoe: the one-GPU share of a sparse mixture-of-experts layer on MI355X (gfx950).
+ *
+ *   y = sum_{i in TopK(G(x), k)} g_i(x) * Expert_i(x)
+ *
+ * The layer runs as five steps, each an entry point below, all enqueued on the caller's HIP stream:
+ *   moe_route              router logits, top-k selection, gate values
+ *   moe_dispatch_layout    per-expert / per-rank counts and offsets, the stable permutation
+ *   moe_permute            copy each kept (token, expert) pair's row into its expert's contiguous group
+ *   moe_expert_ffn         grouped expert FFN over the contiguous groups (= ffn_up then ffn_down)
+ *   moe_unpermute_combine  reverse permutation and gate-weighted sum of each token's k outputs
+ *
+ * Pages cited (titles as the pages give them):
+ *   [EPA2A] "Expert Parallelism and All-to-All"
+ *   [A2AC]  "Expert Parallelism > All-to-All Communication"
+ *   [COMM]  "Expert Parallelism > Communication Overhead Analysis"
+ *   [EPLLM] "Expert Parallelism in Large Language Models: How All-to-All Token Dispatch, Capacity
+ *           Factors, and Parallel Folding Scale MoE Architectures"
+ *
+ * Conventions, all entry points:
+ *   - Ownership: the caller allocates and owns every buffer (inputs, outputs, workspaces). The
+ *     library never allocates, frees or synchronises; it only enqueues kernels on `stream`.
+ *   - State: none kept between calls; calls on different streams do not interact.
+ *   - Layout: row-major. x[T,D]; W_g[E,D]; W1, W3 [E,F,D]; W2 [E,D,F] (each weight matrix is
+ *     (out, in), so every GEMM operand is contiguous along its reduction dimension).
+ *   - Element type of x, weights, x_perm, h, y_perm, y: dims.dtype (MOE_F32 or MOE_BF16). Router
+ *     logits, bias and gates are always float32; indices and counts are int32.
+ *   - Sizes that depend on the routing (kept rows N, per-expert counts) stay on the device: the
+ *     row-indexed buffers are sized for the worst case N_max = T*top_k rows and kernels read
+ *     N = expert_offsets[E] themselves. The host never waits on the GPU.
+ *   - Pointers to element arrays must be 16-byte aligned.
+ *   - Errors: every entry point returns an int status (MOE_OK = 0). Argument checks run on the host
+ *     before anything is enqueued; MOE_ERR_HIP reports a launch failure (hipGetLastError).
+ *     Device-side preconditions (topk_idx values in [0,E)) are the caller's to keep.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1, /* null required pointer, inconsistent dims, misaligned pointer */
+  MOE_ERR_UNSUPPORTED = 2, /* valid dims this build has no kernel for (see each entry point) */
+  MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than moe_workspace_size() */
+  MOE_ERR_HIP = 4          /* a kernel launch failed */
+};
+
+enum moe_gate {
+  MOE_GATE_SOFTMAX_TOPK = 0, /* g = softmax over the k selected logits ([EPLLM] pipeline step 1) */
+  MOE_GATE_SIGMOID_TOPK = 1, /* g_j = sigmoid(l_j) / sum of sigmoid over the k selected */
+  MOE_GATE_SOFTMAX_FULL = 2  /* g_j = softmax over all E logits at the selected experts */
+};
+
+enum moe_act {
+  MOE_ACT_SWIGLU = 0, /* W2 * (SiLU(W1 h) (*) (W3 h))  -- three matrices per expert */
+  MOE_ACT_GELU = 1    /* W2 * GELU(W1 h), exact erf GELU -- two matrices, w3 unused */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+enum moe_stage { MOE_STAGE_LAYOUT = 0, MOE_STAGE_FFN = 1 };
+
+/* Problem statement of one layer call ([COMM] volume equation: B*S tokens as T, top-k as K,
+ * hidden size D; [EPLLM] capacity equation; [A2AC] expert -> device map).
+ *   T, D, E, top_k, F   tokens, hidden size, experts, experts per token, expert hidden size
+ *   capacity_factor     <= 0: dropless. > 0: C = ceil(capacity_factor * top_k * T / E) rows/expert
+ *   ep_size, ep_rank    emulated expert-parallel size (E % ep_size == 0; rank r owns experts
+ *                       [r*E/ep_size, (r+1)*E/ep_size)); ep_rank only labels the local rank
+ *   n_groups, topk_groups  0: no group limit. Otherwise experts form n_groups contiguous groups and
+ *                       each token may only pick experts of its topk_groups best groups
+ *                       ([EPA2A] node-limited routing); a group's score is the sum of its
+ *                       top_k/topk_groups best member scores (sigmoid scores under
+ *                       MOE_GATE_SIGMOID_TOPK, logits otherwise)
+ *   gate, act, dtype    enum moe_gate, enum moe_act, enum moe_dtype */
+typedef struct moe_dims {
+  int32_t T, D, E, top_k, F;
+  int32_t ep_size, ep_rank;
+  int32_t n_groups, topk_groups;
+  int32_t gate, act, dtype;
+  double capacity_factor;
+} moe_dims;
+
+/* Expert capacity C ([EPLLM] "Static Capacity Factors and Token Dropping", capacity equation),
+ * evaluated on the host in IEEE double; T*top_k when dropless. Host only. */
+int moe_capacity(const moe_dims* d, int32_t* capacity);
+
+/* Workspace bytes that `stage` needs (MOE_STAGE_LAYOUT: moe_dispatch_layout; MOE_STAGE_FFN:
+ * moe_expert_ffn, which keeps the expert hidden activations h[T*top_k, F] there). Host only. */
+int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes);
+
+/* Router ([EPLLM] "The Execution Pipeline" step 1; layer equation of "The Distributed MoE Dilemma").
+ *   x [T,D] dtype; w_gate [E,D] dtype; bias [E] float32 or NULL (added to every token's logits).
+ *   topk_idx [T,top_k] int32 out: slot j = the (j+1)-th best expert by (-logit, expert index), so
+ *     exact ties go to the lower index; with a group limit only experts of kept groups qualify.
+ *   topk_gate [T,top_k] float32 out: gate values per enum moe_gate.
+ *   logits [T,E] float32 out, or NULL: the float32 logits the selection was taken on.
+ * Logits are accumulated and kept in float32. Unsupported: E > 256, top_k > 32, D % 8 != 0. */
+int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias,
+              int32_t* topk_idx, float* topk_gate, float* logits, hipStream_t stream);
+
+/* Dispatch layout ([EPA2A] "The two exchanges": each device sorts its tokens by destination
+ * expert; [EPLLM] pipeline steps 1-2: replicate each token k times tagged with expert and rank,
+ * group them contiguously per rank; [A2AC] send counts per device).
+ * Pair id p = t*top_k + j. Rows are ordered by (expert, p): stable. With a capacity C an expert
+ * keeps its first C pairs in p order and drops the rest. Outputs (int32, device):
+ *   expert_counts [E]     pairs routed to each expert before the capacity cut
+ *   expert_offsets [E+1]  first row of each expert's kept group; expert_offsets[E] = N kept rows
+ *   rank_counts [ep_size] kept rows bound for each emulated rank (the all-to-all send counts)
+ *   rank_offsets [ep_size+1] first row of each rank's send chunk
+ *   pair_to_row [T*top_k] row of pair p, or -1 when dropped
+ *   row_to_pair [T*top_k] pair held by row r for r < N, -1 for r >= N
+ *   ws, ws_bytes          scratch of moe_workspace_size(MOE_STAGE_LAYOUT) bytes
+ * Deterministic: the result does not depend on the order in which the GPU runs its threads. */
+int moe_dispatch_layout(const moe_dims* d, const int32_t* topk_idx, int32_t* expert_counts,
+                        int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                        int32_t* pair_to_row, int32_t* row_to_pair, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Permute ([EPLLM] pipeline step 2): x_perm[pair_to_row[t*k+j]] = x[t] for every kept pair.
+ *   x [T,D] dtype in; pair_to_row [T*top_k] int32 in; x_perm [T*top_k, D] dtype out (rows >= N are
+ *   left untouched). A bit-exact copy; each x row is read once. */
+int moe_permute(const moe_dims* d, const void* x, const int32_t* pair_to_row, void* x_perm,
+                hipStream_t stream);
+
+/* Grouped expert FFN ([EPLLM] pipeline step 4: one batched GEMM per local expert over all of its
+ * rows; expert = W2 * (SiLU(W1 h) (*) (W3 h)), or W2 * GELU(W1 h)). Rows [expert_offsets[e],
+ * expert_offsets[e+1]) of x_perm go through expert e; no padding and no dropping.
+ *   x_perm [T*top_k, D] in; w1, w3 [E,F,D]; w2 [E,D,F]; w3 may be NULL for MOE_ACT_GELU.
+ *   y_perm [T*top_k, D] out (rows >= N untouched); ws: moe_workspace_size(MOE_STAGE_FFN) bytes.
+ * bf16: matrix-core products with float32 accumulation; h is rounded to bf16 between the two
+ * GEMMs; outputs rounded to nearest even. Unsupported: D or F not a multiple of 64. */
+int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
+                   const void* w1, const void* w3, const void* w2, void* y_perm, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* First half of moe_expert_ffn: h[r] = act(W1[e] x_perm[r], W3[e] x_perm[r]) for each kept row r of
+ * expert e.  h [T*top_k, F] dtype out (rows >= N untouched). Same rules as moe_expert_ffn. */
+int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
+                      const void* w1, const void* w3, void* h, hipStream_t stream);
+
+/* Second half of moe_expert_ffn: y_perm[r] = W2[e] h[r]. h [T*top_k, F] in; y_perm [T*top_k, D] out. */
+int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_offsets,
+                        const void* w2, void* y_perm, hipStream_t stream);
+
+/* Unpermute + combine ([EPLLM] pipeline step 6: restore order, weight each of the k expert
+ * outputs by its gate and sum; the residual is left to the caller):
+ *   y[t] = sum over slots j with pair_to_row[t*k+j] >= 0 of topk_gate[t*k+j] * y_perm[row].
+ * Sums in float32 in slot order, rounds once. A token whose pairs were all dropped gets 0.
+ *   y_perm [T*top_k, D] dtype in; pair_to_row, topk_gate [T*top_k]; y [T,D] dtype out. */
+int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row,
+                          const float* topk_gate, void* y, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_str(int status);
+
+/* ABI version of this header (major*100 + minor). */
+int moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

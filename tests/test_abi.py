@@ -1,0 +1,131 @@
+"""Host-side checks of libmoe's C ABI: it loads, exports every declared entry point, and its host
+logic (capacity, workspace sizes, argument validation) behaves. No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_experts_amd as M
+from combine_experts_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load_library()
+    names = _declared_functions()
+    assert len(names) >= 11, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in moe.h but not exported"
+    assert set(names) == set(L._SIG), "binding and header disagree"
+
+
+def test_abi_version_and_status_strings():
+    assert M.moe_abi_version() == 100
+    for s in range(5):
+        assert M.moe_status_str(s).startswith("MOE_")
+    assert "unknown" in M.moe_status_str(99)
+
+
+def test_struct_layout_matches_header():
+    # 12 int32 fields then one double: 48 + 8 bytes, double at offset 48
+    assert ctypes.sizeof(M.moe_dims) == 56
+    assert M.moe_dims.capacity_factor.offset == 48
+
+
+def test_capacity_matches_closed_form():
+    d = M.make_dims(4096, 1024, 16, 1, 4096, capacity_factor=1.25, act=M.MOE_ACT_GELU)
+    assert M.moe_capacity(d) == 320
+    d = M.make_dims(4096, 1024, 8, 2, 4096, capacity_factor=1.0)
+    assert M.moe_capacity(d) == 1024
+    d = M.make_dims(1000, 64, 7, 2, 64, capacity_factor=1.5)
+    assert M.moe_capacity(d) == 429
+    d = M.make_dims(100, 64, 4, 2, 64)          # dropless
+    assert M.moe_capacity(d) == 200
+    d = M.make_dims(100, 64, 4, 2, 64, capacity_factor=1000.0)  # capped at T*k
+    assert M.moe_capacity(d) == 200
+
+
+def test_workspace_sizes():
+    d = M.make_dims(16384, 7168, 256, 8, 2048)
+    assert M.moe_workspace_size(d, M.MOE_STAGE_FFN) >= 16384 * 8 * 2048 * 2
+    assert M.moe_workspace_size(d, M.MOE_STAGE_LAYOUT) >= 256 * 4
+    with pytest.raises(M.MoEError) as ei:
+        M.moe_workspace_size(d, 7)
+    assert ei.value.status == M.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_k=0), dict(top_k=9), dict(E=8, ep_size=3), dict(ep_rank=4, ep_size=4),
+    dict(n_groups=3), dict(n_groups=4, topk_groups=0), dict(n_groups=4, topk_groups=5),
+    dict(n_groups=4, topk_groups=1, top_k=3), dict(gate=7), dict(act=5), dict(dtype=9), dict(D=0),
+    dict(T=-1), dict(capacity_factor=float("nan")),
+])
+def test_invalid_dims_rejected_on_host(kw):
+    base = dict(T=16, D=64, E=8, top_k=2, F=64, ep_size=4)
+    base.update(kw)
+    d = M.make_dims(base.pop("T"), base.pop("D"), base.pop("E"), base.pop("top_k"), base.pop("F"), **base)
+    lib = M.load_library()
+    c = ctypes.c_int32()
+    assert lib.moe_capacity(ctypes.byref(d), ctypes.byref(c)) == M.MOE_ERR_INVALID_ARG
+    # entry points reject before touching the device, even with null pointers
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute(ctypes.byref(d), None, None, None, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_null_and_misaligned_pointers_rejected():
+    lib = M.load_library()
+    d = M.make_dims(16, 64, 8, 2, 64)
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    fake = 0x1000
+    assert lib.moe_permute(ctypes.byref(d), fake + 2, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_unpermute_combine(ctypes.byref(d), fake, fake, fake, fake + 8, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_up(ctypes.byref(d), fake, fake, fake, None, fake, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_unsupported_shapes_reported():
+    lib = M.load_library()
+    fake = 0x1000
+    d = M.make_dims(16, 64, 512, 2, 64)                    # E beyond the router's 256
+    assert lib.moe_route(ctypes.byref(d), fake, fake, None, fake, fake, None, None) == M.MOE_ERR_UNSUPPORTED
+    d = M.make_dims(16, 96, 8, 2, 64)                      # bf16 FFN needs D % 64 == 0
+    assert lib.moe_expert_ffn_up(ctypes.byref(d), fake, fake, fake, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_checks():
+    lib = M.load_library()
+    fake = 0x1000
+    d = M.make_dims(1000, 64, 8, 2, 64)
+    need = M.moe_workspace_size(d, M.MOE_STAGE_LAYOUT)
+    args = [fake] * 7
+    assert lib.moe_dispatch_layout(ctypes.byref(d), *args, None, need, None) == M.MOE_ERR_WORKSPACE
+    assert lib.moe_dispatch_layout(ctypes.byref(d), *args, fake, need - 1, None) == M.MOE_ERR_WORKSPACE
+    ffn_need = M.moe_workspace_size(d, M.MOE_STAGE_FFN)
+    assert lib.moe_expert_ffn(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, ffn_need - 1,
+                              None) == M.MOE_ERR_WORKSPACE
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    d = M.make_dims(4, 64, 8, 2, 64)
+    with pytest.raises(ValueError):
+        M.moe_permute(d, torch.zeros(4, 64, dtype=torch.bfloat16), torch.zeros(8, dtype=torch.int32),
+                      torch.zeros(8, 64, dtype=torch.bfloat16))
+
+
+def test_product_path_does_not_import_oracle():
+    # the library package and the oracle share no code: nothing under combine_experts_amd names it
+    pkg = os.path.join(ROOT, "combine_experts_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
