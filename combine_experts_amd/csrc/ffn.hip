@@ -12,10 +12,10 @@
 // Both operands are contiguous along K (weights are (out, in)), which is what the matrix cores
 // want: each lane feeds 8 consecutive K elements (16 bytes) per operand per instruction.
 //
-// Tile map: blockIdx.y = output column tile, blockIdx.x = a slot in the concatenation of every
-// expert's row tiles. Each block derives its (expert, row tile) from expert_offsets with a block
-// scan of ceil(rows_e / BM); slots past the last tile exit. The grid is sized for the worst case
-// (N_max / BM + E slots), so the host never reads counts.
+// Every block derives its tile from expert_offsets (a block scan of the per-expert tile counts); the
+// grid is sized for the worst case (N_max / BM + E row tiles per column tile) and blocks past the
+// last tile exit, so the host never reads counts. The bf16 path is described above its kernel;
+// the float32 path (small workloads only) is a plain LDS-tiled FMA GEMM on a 2-D grid.
 #include "moe_common.h"
 
 namespace moe {
@@ -75,135 +75,264 @@ __device__ bool map_tile(const int32_t* __restrict__ offsets, int E, int slot, i
   return true;
 }
 
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
-
 __device__ __forceinline__ float act_silu(float a) { return a / (1.f + expf(-a)); }
 __device__ __forceinline__ float act_gelu(float a) { return 0.5f * a * (1.f + erff(a * 0.70710678118654752f)); }
+// SiLU with the hardware exp2 and reciprocal (relative error a few float32 ulp; the result is rounded to bf16)
+__device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_amdgcn_rcpf(1.f + __expf(-a)); }
 
 // ---------------------------------------------------------------------------------------------------
-// bf16 grouped GEMM on matrix cores. BM x BN output tile per B matrix (two B matrices for SwiGLU),
-// BK = 64, 4 waves in a 2 x 2 grid, each wave a 64 x 64 sub-tile of 2 x 2 32x32x16 MFMA blocks.
-// LDS: double-buffered A and B tiles of 16-byte chunks, 8 chunks per 64-wide row, XOR-swizzled.
+// bf16 grouped GEMM on matrix cores.
+//
+// Block: 8 waves (2 per SIMD) own a 256-row x 256-B-row tile; for SwiGLU the 256 B rows are 128
+// rows of W1 and the matching 128 rows of W3, so the block produces 256 x 128 of h. Wave (wm, wn)
+// holds m-blocks {2i + wm} (32 rows each, interleaved so a ragged tile splits evenly between the
+// two wave rows) against 2 B blocks of 32 rows: 8 v_mfma_f32_32x32x16_bf16 per 16-deep k-step,
+// accumulators 4 x 2 x 16 floats. The weight fragment is the MFMA's first operand, so each lane
+// ends up with 4 consecutive output columns of one token row: 8-byte stores in the epilogue.
+//
+// K runs in 64-deep stages through a 2-slot LDS ring (64 KB per slot). Loads go straight from
+// global memory into LDS (16 bytes per lane, no register staging) and are issued two per k-step,
+// one stage ahead. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
+// ch ^ ((row >> 1) & 7), so the 32 rows one fragment read touches fall on distinct banks.
+//
+// Tile order: a block's tile comes from its index through an XCD-aware map (workgroups are handed
+// to the 8 XCDs round robin): XCD x takes a contiguous range of the expert-major tile list, so
+// the tiles of one expert run together on one XCD and share its L2 (each x_perm row and weight
+// row is fetched from HBM about once). Within an expert, tiles go in groups of 8 column tiles,
+// row-tile-major inside a group. Rows past the expert's count are loaded from row 0 (finite
+// values) and never stored; 32-row blocks entirely past the count are not multiplied.
 // ---------------------------------------------------------------------------------------------------
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int KCH = BK / 8;  // 16-byte chunks per tile row
+constexpr int GW = 8, GTH = GW * MOE_WAVE;        // waves / threads per block
+constexpr int GBM = 256, GBR = 256, GBK = 64;      // tile rows, B rows per tile, K per stage
+constexpr int GKCH = GBK / 8;                       // 16-byte chunks per tile row
+constexpr int G_ACH = GBM * GKCH, G_STAGE = (GBM + GBR) * GKCH, G_LPS = G_STAGE / GTH, G_KS = GBK / 16;
+constexpr int G_GN = 8;                             // column tiles per group in the tile order
 
-template <int ACT, bool DUAL>
-__global__ void __launch_bounds__(256) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-                                                     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                     bf16_t* __restrict__ out, int E, int K, int Nout) {
-  constexpr int NB = DUAL ? 2 : 1;
-  constexpr int A_CH = BM * KCH, B_CH = BN * KCH;
-  constexpr int STAGE = A_CH + NB * B_CH;
-  __shared__ bf16x8 lds[2 * STAGE];
+__device__ __forceinline__ int gswz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
 
-  int e, row0, mrows;
-  if (!map_tile<BM>(offsets, E, blockIdx.x, &e, &row0, &mrows)) return;
-  const int n0 = blockIdx.y * BN;
-  const int tid = threadIdx.x, lane = tid % MOE_WAVE, wave = tid / MOE_WAVE;
-  const int wm = wave / 2, wn = wave % 2;
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
 
-  const bf16_t* Ab = A + (size_t)row0 * K;
-  const bf16_t* Bb[NB];
-  Bb[0] = B0 + ((size_t)e * Nout + n0) * K;
-  if constexpr (DUAL) Bb[NB - 1] = B1 + ((size_t)e * Nout + n0) * K;
-
-  // global -> register staging: 4 A chunks and 4 chunks per B matrix per thread per K tile
-  bf16x8 ra[A_CH / 256], rb[NB][B_CH / 256];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+__device__ __forceinline__ int block_scan_g(int v, int* lds, int* total) {
+  const int lane = threadIdx.x % MOE_WAVE, wave = threadIdx.x / MOE_WAVE;
+  int inc = v;
 #pragma unroll
-    for (int i = 0; i < A_CH / 256; ++i) {
-      const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
-      ra[i] = (row < mrows) ? *reinterpret_cast<const bf16x8*>(Ab + (size_t)row * K + k0 + ch * 8) : bf16x8{};
-    }
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int i = 0; i < B_CH / 256; ++i) {
-        const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
-        rb[m][i] = (n0 + row < Nout) ? *reinterpret_cast<const bf16x8*>(Bb[m] + (size_t)row * K + k0 + ch * 8)
-                                     : bf16x8{};
-      }
-  };
-  auto sstore = [&](int buf) {
-    bf16x8* s = lds + buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < A_CH / 256; ++i) {
-      const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
-      s[row * KCH + swz(row, ch)] = ra[i];
-    }
-#pragma unroll
-    for (int m = 0; m < NB; ++m)
-#pragma unroll
-      for (int i = 0; i < B_CH / 256; ++i) {
-        const int c = tid + i * 256, row = c / KCH, ch = c % KCH;
-        s[A_CH + m * B_CH + row * KCH + swz(row, ch)] = rb[m][i];
-      }
-  };
-
-  f32x16 acc[NB][2][2];
-#pragma unroll
-  for (int m = 0; m < NB; ++m)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[m][i][j][v] = 0.f;
-
-  const int nk = K / BK;
-  gload(0);
-  sstore(0);
+  for (int off = 1; off < MOE_WAVE; off <<= 1) {
+    const int u = __shfl_up(inc, off, MOE_WAVE);
+    if (lane >= off) inc += u;
+  }
   __syncthreads();
+  if (lane == MOE_WAVE - 1) lds[wave] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < GW; ++w) {
+    const int x = lds[w];
+    if (w < wave) before += x;
+    tot += x;
+  }
+  *total = tot;
+  return before + inc - v;
+}
+
+// This block's (expert, row tile, column tile), or false when it has none.
+__device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT, int* e_out, int* mt_out,
+                             int* nt_out) {
+  __shared__ int s_tmp[GW];
+  __shared__ int s_e, s_local;
+  int L = 0;  // total tiles
+  for (int base = 0; base < E; base += GTH) {
+    const int e = base + threadIdx.x;
+    const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    int tot;
+    block_scan_g(((cnt + GBM - 1) / GBM) * NT, s_tmp, &tot);
+    L += tot;
+  }
+  const int per = (L + 7) / 8;
+  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  if (j >= per) return false;
+  const int t = xcd * per + j;
+  if (t >= L) return false;
+  if (threadIdx.x == 0) s_e = -1;
+  int carry = 0;
+  for (int base = 0; base < E; base += GTH) {
+    const int e = base + threadIdx.x;
+    const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const int n = ((cnt + GBM - 1) / GBM) * NT;
+    int tot;
+    const int start = carry + block_scan_g(n, s_tmp, &tot);
+    if (e < E && t >= start && t < start + n) {
+      s_e = e;
+      s_local = t - start;
+    }
+    carry += tot;
+    if (carry > t) break;  // uniform across the block
+  }
+  __syncthreads();
+  const int e = s_e;
+  const int MT = (offsets[e + 1] - offsets[e] + GBM - 1) / GBM;
+  const int gsz = G_GN * MT;
+  const int g = s_local / gsz, r = s_local % gsz;
+  const int gn = min(G_GN, NT - g * G_GN);
+  *e_out = e;
+  *mt_out = r / gn;
+  *nt_out = g * G_GN + r % gn;
+  return true;
+}
+
+// B-tile row of the wave's j-th 32-row block
+template <bool DUAL>
+__device__ __forceinline__ int gbrow(int wn, int j) {
+  if constexpr (DUAL) return j == 0 ? wn * 32 : GBR / 2 + wn * 32;
+  else return wn * 64 + j * 32;
+}
+
+template <int ACT>  // active 32-row blocks of this wave
+__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
+                                           const int (&aoff)[G_KS][4], const int (&boff)[G_KS][2], int wave, int nk) {
+  auto issue = [&](int kt, int buf, int i) {
+    __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * GBK),
+                                     (__attribute__((address_space(3))) void*)(lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE),
+                                     16, 0, 0);
+  };
+  bf16x8 fa[2][4], fb[2][2];
+  auto frag = [&](int buf, int ks, int r) {
+    const bf16x8* s = lds + buf * G_STAGE;
+#pragma unroll
+    for (int i = 0; i < ACT; ++i) fa[r][i] = s[aoff[ks][i]];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) fb[r][j] = s[boff[ks][j]];
+  };
+#pragma unroll
+  for (int i = 0; i < G_LPS; ++i) issue(0, 0, i);
+  wait_vmcnt<0>();
+  __syncthreads();
+  frag(0, 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const bf16x8* s = lds + buf * STAGE;
+    const bool refill = kt + 1 < nk;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + lane / 32;
-      bf16x8 a[2], b[NB][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + lane % 32;
-        a[i] = s[row * KCH + swz(row, ch)];
+    for (int ks = 0; ks < G_KS; ++ks) {
+      const int c = ks & 1, n = c ^ 1;
+      // stage kt+1 goes to the other slot, free since the barrier that ended iteration kt-1
+      if (refill) {
+        issue(kt + 1, buf ^ 1, 2 * ks);
+        issue(kt + 1, buf ^ 1, 2 * ks + 1);
+      }
+      if (ks < G_KS - 1) {
+        frag(buf, ks + 1, n);
+      } else if (refill) {
+        wait_vmcnt<0>();  // this wave's part of stage kt+1 has landed ...
+        __syncthreads();  // ... and everyone's; everyone is also done reading slot buf
+        frag(buf ^ 1, 0, n);
       }
 #pragma unroll
-      for (int m = 0; m < NB; ++m)
+      for (int i = 0; i < ACT; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int row = wn * 64 + j * 32 + lane % 32;
-          b[m][j] = s[A_CH + m * B_CH + row * KCH + swz(row, ch)];
-        }
-#pragma unroll
-      for (int m = 0; m < NB; ++m)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[m][j], acc[m][i][j], 0, 0, 0);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][j], fa[c][i], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
-    __syncthreads();
   }
+}
 
-  // epilogue: lane holds C[i][j] for j = lane%32, i = (v/4)*8 + (lane/32)*4 + v%4
+template <int ACTFN, bool DUAL>
+__global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
+                                                     const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
+                                                     bf16_t* __restrict__ out, int E, int K, int Nout) {
+  constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
+  __shared__ bf16x8 lds[2 * G_STAGE];
+  const int NT = (Nout + BNO - 1) / BNO;
+  int e, mt, nt;
+  if (!map_tile_xcd(offsets, E, NT, &e, &mt, &nt)) return;
+  const int row0 = offsets[e] + mt * GBM;
+  const int mrows = min(GBM, offsets[e + 1] - row0);
+  const int n0 = nt * BNO;
+  const int lane = threadIdx.x % MOE_WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
+  const int wm = wave / 4, wn = wave % 4;
+  const bf16_t* Ab = A + (size_t)row0 * K;
+  const bf16_t* Bw0 = B0 + ((size_t)e * Nout + n0) * K;
+  const bf16_t* Bw1 = DUAL ? B1 + ((size_t)e * Nout + n0) * K : nullptr;
+
+  // source of each of this lane's direct loads: load i fills LDS slots [i*GTH + wave*64, +64)
+  const bf16_t* src[G_LPS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < G_LPS; ++i) {
+    const int slot = i * GTH + wave * MOE_WAVE + lane;
+    if (i * GTH < G_ACH) {
+      const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
+      src[i] = Ab + (size_t)(row < mrows ? row : 0) * K + ch * 8;
+    } else {
+      const int bs = slot - G_ACH;
+      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
+      const bf16_t* p;
+      if constexpr (DUAL) {
+        const int f = row % (GBR / 2);
+        p = (n0 + f < Nout) ? ((row < GBR / 2 ? Bw0 : Bw1) + (size_t)f * K) : Bw0;
+      } else {
+        p = (n0 + row < Nout) ? Bw0 + (size_t)row * K : Bw0;
+      }
+      src[i] = p + ch * 8;
+    }
+  }
+  int aoff[G_KS][4], boff[G_KS][2];
+#pragma unroll
+  for (int ks = 0; ks < G_KS; ++ks) {
+    const int ch = ks * 2 + lane / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (2 * i + wm) * 32 + lane % 32;
+      aoff[ks][i] = row * GKCH + gswz(row, ch);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = gbrow<DUAL>(wn, j) + lane % 32;
+      boff[ks][j] = G_ACH + row * GKCH + gswz(row, ch);
+    }
+  }
+  const int nblk = (mrows + 31) / 32;
+  const int act = __builtin_amdgcn_readfirstlane((nblk - wm + 1) / 2);  // blocks 2i+wm < nblk
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = wm * 64 + i * 32 + (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-        const int c = n0 + wn * 64 + j * 32 + lane % 32;
-        if (r < mrows && c < Nout) {
-          float h = acc[0][i][j][v];
-          if constexpr (ACT == MOE_ACT_SWIGLU && DUAL) h = act_silu(h) * acc[NB - 1][i][j][v];
-          else if constexpr (ACT == MOE_ACT_GELU) h = act_gelu(h);
-          out[(size_t)(row0 + r) * Nout + c] = f2bf(h);
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  const int nk = K / GBK;
+  // every wave runs the same stages and barriers; a wave with no rows multiplies one block
+  switch (act) {
+    case 4: gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk); break;
+    case 3: gemm_kloop<3>(acc, lds, src, aoff, boff, wave, nk); break;
+    case 2: gemm_kloop<2>(acc, lds, src, aoff, boff, wave, nk); break;
+    default: gemm_kloop<1>(acc, lds, src, aoff, boff, wave, nk); break;
+  }
+  // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (2 * i + wm) * 32 + lane % 32;
+    if (i >= act || r >= mrows) continue;
+    bf16_t* orow = out + (size_t)(row0 + r) * Nout + n0;
+#pragma unroll
+    for (int j = 0; j < (DUAL ? 1 : 2); ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = (DUAL ? wn * 32 : wn * 64 + j * 32) + 8 * q + 4 * (lane / 32);
+        if (n0 + c >= Nout) continue;
+        bf16x4 pk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float h = acc[i][j][4 * q + u];
+          if constexpr (ACTFN == MOE_ACT_SWIGLU && DUAL) h = act_silu_fast(h) * acc[i][1][4 * q + u];
+          else if constexpr (ACTFN == MOE_ACT_GELU) h = act_gelu(h);
+          pk[u] = f2bf(h);
         }
+        *reinterpret_cast<bf16x4*>(orow + c) = pk;
       }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------------
@@ -278,19 +407,21 @@ dim3 ffn_grid(const FfnArgs& a, int tbn) {
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   if (a.n_rows_max == 0) return hipSuccess;
-  const dim3 grid = ffn_grid<BM>(a, BN);
+  const int bno = a.act == MOE_ACT_SWIGLU ? GBR / 2 : GBR;
+  const long long row_tiles = (a.n_rows_max + GBM - 1) / GBM + (a.E < a.n_rows_max ? a.E : a.n_rows_max);
+  const dim3 grid((unsigned)(row_tiles * ((a.Nout + bno - 1) / bno) + 8));
   const bf16_t* A = (const bf16_t*)a.a;
   const bf16_t* b0 = (const bf16_t*)a.b0;
   const bf16_t* b1 = (const bf16_t*)a.b1;
   bf16_t* o = (bf16_t*)a.out;
   if (a.act == MOE_ACT_SWIGLU)
-    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_SWIGLU, true>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o,
+    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_SWIGLU, true>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o,
                        a.E, a.K, a.Nout);
   else if (a.act == MOE_ACT_GELU)
-    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_GELU, false>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o,
+    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_GELU, false>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o,
                        a.E, a.K, a.Nout);
   else
-    hipLaunchKernelGGL((ffn_gemm_bf16<-1, false>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o, a.E, a.K,
+    hipLaunchKernelGGL((ffn_gemm_bf16<-1, false>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, a.K,
                        a.Nout);
   return hipGetLastError();
 }

@@ -105,6 +105,7 @@ int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float*
   if (!aligned16(x) || !aligned16(w_gate) || !aligned4(topk_idx) || !aligned4(topk_gate)) return MOE_ERR_INVALID_ARG;
   if ((bias && !aligned4(bias)) || (logits && !aligned4(logits))) return MOE_ERR_INVALID_ARG;
   if (d->E > 256 || d->top_k > 32 || d->D % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d->dtype == MOE_BF16 && d->D % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->n_groups > 64 || (d->n_groups > 0 && d->top_k / d->topk_groups > 8)) return MOE_ERR_UNSUPPORTED;
   moe::RouteArgs a{x, w_gate, bias, topk_idx, topk_gate, logits, d->T, d->D, d->E, d->top_k,
                    d->n_groups, d->n_groups > 0 ? d->topk_groups : 0, d->gate};

@@ -9,9 +9,10 @@
 // One block = 4 waves = 64 tokens; all E (<= 256) experts of a token stay in one block, so the
 // selection needs no second pass over HBM.
 //   bf16: matrix cores (v_mfma_f32_16x16x32_bf16) with float32 accumulation. Each wave owns 16
-//         tokens; the block stages a 64-wide K slice of W_g for all experts in LDS (double
-//         buffered, 16-byte chunks XOR-swizzled against bank conflicts); x fragments come straight
-//         from HBM (each x element is read once).
+//         tokens; the block streams 64-wide K slices of W_g for all experts through an LDS ring
+//         (direct global->LDS loads, 16-byte chunks XOR-swizzled against bank conflicts) while x
+//         fragments stream from HBM into registers, four slices in flight (the step is bound by
+//         HBM bandwidth on x, so latency must be covered by depth, not by compute).
 //   fp32: plain FMA dot products (the small fp32 workload only).
 // The [64 x E] float32 logit tile then goes to LDS, and each wave selects for its 16 tokens:
 // group scores (if limited), then k rounds of a wave-wide argmax on (value, -index), so exact
@@ -30,59 +31,90 @@ constexpr int kMaxPerLane = kMaxE / MOE_WAVE;
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // ---- logits, bf16 on matrix cores ---------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
+// Streaming K loop, kDepth slices in flight: W_g K-slices go global -> LDS directly (16 bytes per
+// lane; lane i of a load fills LDS chunk base + i) through a kDepth-slot ring; x fragments go into a
+// kDepth-deep register ring with non-temporal loads (each x element is read once; W_g stays in L2).
+// The loop is unrolled by kDepth so ring indices are compile-time. Requires D % 64 == 0.
+constexpr int kDepth = 4;
+
 template <int NT>  // 16-expert MFMA column tiles; experts padded to NT*16
 __device__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* bias,
                             float* lds_logits, char* lds_raw, int T, int D, int E, int t0) {
   constexpr int epad = NT * 16;
+  constexpr int STAGE = epad * (kKC / 8);        // 16-byte chunks per slice
+  constexpr int LPT = (STAGE + 255) / 256;       // direct loads per thread per slice
+  constexpr int PER_STAGE = LPT + 2;             // vector-memory instructions per slice per wave
   const int tid = threadIdx.x;
-  const int wave = tid / MOE_WAVE, lane = tid % MOE_WAVE;
-  bf16x8* wbuf = reinterpret_cast<bf16x8*>(lds_raw);  // [2][epad][8 chunks of 16 B]
-  constexpr int stage_chunks = epad * (kKC / 8);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
+  const int lane = tid % MOE_WAVE;
+  bf16x8* wbuf = reinterpret_cast<bf16x8*>(lds_raw);  // [kDepth][STAGE]
+
+  const bf16_t* wsrc[LPT];
+#pragma unroll
+  for (int i = 0; i < LPT; ++i) {
+    const int slot = i * 256 + wave * MOE_WAVE + lane;
+    const int row = slot / (kKC / 8), ch = swz(row, slot % (kKC / 8));
+    wsrc[i] = wg + (size_t)(row < E ? row : E - 1) * D + ch * 8;  // padded experts reuse a real row
+  }
+  const int r = lane % 16, q = lane / 16;          // MFMA row / k-quarter of this lane
+  const int tok = t0 + wave * kTokPerWave + r;
+  const bf16_t* xrow = x + (size_t)(tok < T ? tok : T - 1) * D + q * 16;  // rows past T: values unused
+  const int n_kc = D / kKC;
+  bf16x8 a[kDepth][2];
+
+  // stage kc -> ring slot kc % kDepth (W) and register set kc % kDepth (x)
+  auto issue = [&](int kc, int slot) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      if (i * 256 + wave * MOE_WAVE < STAGE)  // wave-uniform
+        __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + kc * kKC),
+                                         (__attribute__((address_space(3))) void*)(wbuf + slot * STAGE + i * 256 +
+                                                                                   wave * MOE_WAVE),
+                                         16, 0, 0);
+    a[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(xrow + kc * kKC));
+    a[slot][1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(xrow + kc * kKC + 8));
+  };
 
   f32x4 acc[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int r = lane % 16, q = lane / 16;          // MFMA row / k-quarter of this lane
-  const int tok = t0 + wave * kTokPerWave + r;
-  const bool tok_ok = tok < T;
-  const bf16_t* xrow = x + (size_t)(tok_ok ? tok : 0) * D;
-  const int n_kc = (D + kKC - 1) / kKC;
-
-  auto load_w = [&](int kc, int buf) {
-    for (int c = tid; c < stage_chunks; c += 256) {
-      const int row = c / (kKC / 8), ch = c % (kKC / 8);
-      const int k = kc * kKC + ch * 8;
-      bf16x8 v = {};
-      if (row < E && k < D) v = *reinterpret_cast<const bf16x8*>(wg + (size_t)row * D + k);
-      wbuf[buf * stage_chunks + row * (kKC / 8) + swz(row, ch)] = v;
-    }
-  };
-
-  load_w(0, 0);
-  __syncthreads();
-  for (int kc = 0; kc < n_kc; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < n_kc) load_w(kc + 1, buf ^ 1);
-    // lane (r, q) supplies K elements [q*16, q*16+16) of this slice as two 8-wide MFMA fragments
-    bf16x8 a[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int k = kc * kKC + q * 16 + s * 8;
-      a[s] = (tok_ok && k < D) ? *reinterpret_cast<const bf16x8*>(xrow + k) : bf16x8{};
-    }
-    const bf16x8* wb = wbuf + buf * stage_chunks;
+  for (int st = 0; st < kDepth - 1; ++st)
+    if (st < n_kc) issue(st, st);
+  for (int kc0 = 0; kc0 < n_kc; kc0 += kDepth) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int row = nt * 16 + r;
+    for (int u = 0; u < kDepth; ++u) {
+      const int kc = kc0 + u;
+      if (kc < n_kc) {
+        // slice kc landed (this wave's W loads; x registers are waited on by the compiler) ...
+        const int later = n_kc - 1 - kc;  // slices issued after kc, at most kDepth - 2
+        if (later >= kDepth - 2) wait_vmcnt<(kDepth - 2) * PER_STAGE>();
+        else if (later == 1) wait_vmcnt<PER_STAGE>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // ... for every wave; and every wave is done reading slot (kc-1) % kDepth
+        if (kc + kDepth - 1 < n_kc) issue(kc + kDepth - 1, (u + kDepth - 1) % kDepth);
+        const bf16x8* wb = wbuf + u * STAGE;
+        // lane (r, q) supplies K elements [q*16, q*16+16) of this slice as two 8-wide MFMA fragments
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 b = wb[row * (kKC / 8) + swz(row, q * 2 + s)];
-        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc[nt], 0, 0, 0);
+        for (int nt = 0; nt < NT; ++nt) {
+          const int row = nt * 16 + r;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const bf16x8 b = wb[row * (kKC / 8) + swz(row, q * 2 + s2)];
+            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s2], b, acc[nt], 0, 0, 0);
+          }
+        }
       }
     }
-    __syncthreads();
   }
+  __syncthreads();  // all waves done with the ring before the logit tile reuses the memory
   // acc[nt][i]: token row (lane/16)*4 + i of this wave, expert nt*16 + lane%16
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -143,18 +175,49 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
     v[i] = ok[i] ? lrow[e] : -INFINITY;
   }
   if (n_groups > 0) {
-    // group score = sum of the `per` best member scores; lane g < n_groups scores group g
     const int gsize = E / n_groups;
     const int per = max(1, k / topk_groups);
-    float gs = -INFINITY;
-    if (lane < n_groups) {
+    float gs = -INFINITY;  // lane g < n_groups ends up with group g's score
+    if (gsize <= MOE_WAVE && (gsize & (gsize - 1)) == 0 && E % MOE_WAVE == 0) {
+      // expert e = lane + 64*i sits in lane e%64 of register i, so group g is the lane segment
+      // [(g*gsize) % 64, +gsize) of register (g*gsize)/64: score it with `per` rounds of a
+      // segment-wide max (ties: lowest lane), removing each round's winner.
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i) {
+        if (i >= n_per) break;
+        float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i];
+        float sum = 0.f;
+        for (int rnd = 0; rnd < per; ++rnd) {
+          float m = sv;
+          int ml = lane;
+          for (int off = 1; off < gsize; off <<= 1) {
+            const float om = __shfl_xor(m, off, MOE_WAVE);
+            const int ol = __shfl_xor(ml, off, MOE_WAVE);
+            if (om > m || (om == m && ol < ml)) {
+              m = om;
+              ml = ol;
+            }
+          }
+          sum += m;
+          if (lane == ml) sv = -INFINITY;
+        }
+        // every lane of a segment holds its group's score: hand group g's to lane g
+        for (int g = 0; g < n_groups; ++g) {
+          const int src = (g * gsize) % MOE_WAVE;
+          if ((g * gsize) / MOE_WAVE == i) {
+            const float sg = __shfl(sum, src, MOE_WAVE);
+            if (lane == g) gs = sg;
+          }
+        }
+      }
+    } else if (lane < n_groups) {
+      // general group size: lane g walks its group's members, keeping the `per` best
       float best[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) best[j] = -INFINITY;
       for (int m = 0; m < gsize; ++m) {
         const float lv = lrow[lane * gsize + m];
         float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(lv) : lv;
-        // insert into the descending list best[0..per)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (j < per && sv > best[j]) {
@@ -247,6 +310,149 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
   }
 }
 
+// ---- selection for 4 tokens at once --------------------------------------------------------------
+// Each token of a group of four owns a 16-lane segment; lane L of the segment holds the NT experts
+// [L*NT, L*NT + NT) (NT*16 = padded E). Used when E == 16*NT, k <= 16, and with a group limit
+// when a group is a power-of-two number (<= 16) of whole lanes and there are at most 16 groups.
+template <int NT>
+__device__ bool fast_select_ok(int E, int k, int n_groups) {
+  if (E != NT * 16 || k > 16) return false;
+  if (n_groups == 0) return true;
+  const int gsize = E / n_groups;
+  if (gsize % NT != 0 || n_groups > 16) return false;
+  const int lpg = gsize / NT;
+  return lpg >= 1 && lpg <= 16 && (lpg & (lpg - 1)) == 0;
+}
+
+template <int NT>
+__device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int k, int n_groups, int topk_groups,
+                        int gate, int32_t* out_idx, float* out_gate) {
+  constexpr int epad = NT * 16;
+  const int lane = lane_id();
+  const int seg = lane / 16, L = lane % 16;
+  const bool tok_ok = seg < ntok;
+  const float* lrow = lds_logits + (trow0 + (tok_ok ? seg : 0)) * epad + L * NT;
+  float v[NT];
+  bool ok[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    v[i] = lrow[i];
+    ok[i] = true;
+  }
+  if (n_groups > 0) {
+    const int gsize = E / n_groups;
+    const int lpg = gsize / NT;                   // lanes per group
+    const int per = max(1, k / topk_groups);      // members summed per group (<= 8)
+    // this lane's `per` best member scores, descending
+    float best[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) best[j] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j < per && sv > best[j]) {
+          const float t = best[j];
+          best[j] = sv;
+          sv = t;
+        }
+      }
+    }
+    // merge sorted lists across the lanes of the group
+    for (int off = 1; off < lpg; off <<= 1) {
+      float other[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) other[j] = __shfl_xor(best[j], off, MOE_WAVE);
+      float merged[8];
+      int ia = 0, ib = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float a = -INFINITY, b = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (q == ia) a = best[q];
+          if (q == ib) b = other[q];
+        }
+        const bool take_a = a >= b;
+        merged[j] = take_a ? a : b;
+        ia += take_a ? 1 : 0;
+        ib += take_a ? 0 : 1;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) best[j] = merged[j];
+    }
+    float gs = 0.f;  // group score, in every lane of the group (summed in descending order)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < per) gs += best[j];
+    const int my_g = L / lpg;
+    int rank = 0;
+    for (int g = 0; g < n_groups; ++g) {
+      const float og = __shfl(gs, seg * 16 + g * lpg, MOE_WAVE);
+      if (og > gs || (og == gs && g < my_g)) ++rank;
+    }
+    if (rank >= topk_groups) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) ok[i] = false;
+    }
+  }
+  // k rounds of a segment-wide argmax on (value, -expert); lane j of the segment keeps slot j
+  float my_v = 0.f;
+  int my_e = 0;
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int e = L * NT + i;
+      if (ok[i] && better(bv, be, v[i], e)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, MOE_WAVE);
+      const int oe = __shfl_xor(be, off, MOE_WAVE);
+      if (better(bv, be, ov, oe)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      if (L * NT + i == be) ok[i] = false;
+    if (L == j) {
+      my_v = bv;
+      my_e = be;
+    }
+  }
+  const float v0 = __shfl(my_v, seg * 16, MOE_WAVE);
+  float w = 0.f, denom = 0.f;
+  if (gate == MOE_GATE_SOFTMAX_FULL) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) m = fmaxf(m, v[i]);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, MOE_WAVE));
+    float z = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) z += expf(v[i] - m);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off, MOE_WAVE);
+    w = (L < k) ? expf(my_v - m) : 0.f;
+    denom = z;
+  } else {
+    if (L < k) w = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(my_v) : expf(my_v - v0);
+    for (int j = 0; j < k; ++j) denom += __shfl(w, seg * 16 + j, MOE_WAVE);  // slot order
+  }
+  if (tok_ok && L < k) {
+    out_idx[seg * k + L] = my_e;
+    out_gate[seg * k + L] = w / denom;
+  }
+}
+
 template <typename T, int NT>
 __global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                     const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
@@ -272,12 +478,22 @@ __global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, con
       for (int e = lane; e < E; e += MOE_WAVE) logits[(size_t)tok * E + e] = lds_logits[trow * epad + e];
     }
   }
-  for (int i = 0; i < kTokPerWave; ++i) {
-    const int trow = wave * kTokPerWave + i;
-    const int tok = t0 + trow;
-    if (tok >= T_) break;
-    select_token(lds_logits + trow * epad, E, k, n_groups, topk_groups, gate, topk_idx + (size_t)tok * k,
-                 topk_gate + (size_t)tok * k);
+  if (fast_select_ok<NT>(E, k, n_groups)) {
+    for (int i = 0; i < kTokPerWave; i += 4) {
+      const int trow = wave * kTokPerWave + i;
+      const int tok = t0 + trow;
+      if (tok >= T_) break;
+      select4<NT>(lds_logits, trow, min(4, T_ - tok), E, k, n_groups, topk_groups, gate, topk_idx + (size_t)tok * k,
+                  topk_gate + (size_t)tok * k);
+    }
+  } else {
+    for (int i = 0; i < kTokPerWave; ++i) {
+      const int trow = wave * kTokPerWave + i;
+      const int tok = t0 + trow;
+      if (tok >= T_) break;
+      select_token(lds_logits + trow * epad, E, k, n_groups, topk_groups, gate, topk_idx + (size_t)tok * k,
+                   topk_gate + (size_t)tok * k);
+    }
   }
 }
 
@@ -287,8 +503,12 @@ hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
   const int blocks = (a.T + kTokPerBlock - 1) / kTokPerBlock;
   const size_t lds_logits = (size_t)kTokPerBlock * epad * sizeof(float);
   if (dtype == MOE_BF16) {
-    const size_t lds_w = (size_t)2 * epad * kKC * sizeof(bf16_t);
+    const size_t lds_w = (size_t)kDepth * epad * kKC * sizeof(bf16_t);
     const size_t lds = lds_w > lds_logits ? lds_w : lds_logits;
+    // dynamic LDS above the default 64 KB needs the per-kernel limit raised (once per process)
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<bf16_t, NT>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL((route_kernel<bf16_t, NT>), dim3(blocks), dim3(256), lds, s, (const bf16_t*)a.x,
                        (const bf16_t*)a.w_gate, a.bias, a.topk_idx, a.topk_gate, a.logits, a.T, a.D, a.E, a.k,
                        a.n_groups, a.topk_groups, a.gate);

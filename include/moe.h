@@ -101,7 +101,8 @@ int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes);
  *     exact ties go to the lower index; with a group limit only experts of kept groups qualify.
  *   topk_gate [T,top_k] float32 out: gate values per enum moe_gate.
  *   logits [T,E] float32 out, or NULL: the float32 logits the selection was taken on.
- * Logits are accumulated and kept in float32. Unsupported: E > 256, top_k > 32, D % 8 != 0. */
+ * Logits are accumulated and kept in float32. Unsupported: E > 256, top_k > 32, D % 8 != 0, and
+ * for MOE_BF16 D % 64 != 0. */
 int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias,
               int32_t* topk_idx, float* topk_gate, float* logits, hipStream_t stream);
 
