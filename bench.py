@@ -98,6 +98,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--copy-calib-bytes", type=int, default=0,
+                    help="before the timed steps, copy a buffer of this many bytes 3 times (a plain copy kernel "
+                         "of known size, to scale HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -144,6 +147,13 @@ def main(argv=None):
         if ev is not None:
             ev[6].record(stream)
 
+    if args.copy_calib_bytes > 0:
+        src = torch.ones(args.copy_calib_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
