@@ -22,6 +22,7 @@ __all__ = [
     "group_scores", "gate_weights", "route", "decisive_tokens", "capacity", "dispatch_layout",
     "send_counts", "dispatch_matrix", "permute", "silu", "gelu", "expert_ffn", "expert_ffn_rows",
     "combine", "comm_volume_elements", "dispatch_volume_bytes", "layer_forward",
+    "router_probabilities", "load_balance_stats", "update_select_bias",
 ]
 
 GATE_SOFTMAX_TOPK = 0
@@ -147,17 +148,35 @@ def gate_weights(l: np.ndarray, topk_idx: np.ndarray, mode: int) -> np.ndarray:
     raise ValueError(f"unknown gate mode {mode}")
 
 
-def route(x, w_gate, bias, k: int, gate: int, n_groups: int = 0, topk_groups: int = 0) -> Dict[str, np.ndarray]:
+def route(x, w_gate, bias, k: int, gate: int, n_groups: int = 0, topk_groups: int = 0,
+          select_bias=None) -> Dict[str, np.ndarray]:
     """Router step end to end: logits, selection, gates.
 
     Selection decisions are taken on the logits rounded to float32, the
     precision the GPU kernel decides in; exact float32 ties go to the lowest
     expert index. Gate values use the float64 logits.
+
+    ``select_bias`` (optional, [E]): a per-expert bias that moves the selection
+    only, never the gate values -- the bias-adjusted routing scores of
+    aux-loss-free balancing ([CH10] section 4; [EPLLM] "Modern Dropless
+    Dynamic Dispatch"). READING: it is added to the score the selection ranks
+    by (the sigmoid score under sigmoid gating, the logit otherwise), in
+    float32, and group scores are taken on the biased scores.
     """
     l64 = route_logits(x, w_gate, bias)
     l32 = round_to_f32(l64)
     kept_groups = None
-    if n_groups and n_groups > 0:
+    if select_bias is not None:
+        b = np.asarray(as_f64(select_bias), dtype=np.float64)[None, :]
+        if gate == GATE_SIGMOID_TOPK:
+            key = round_to_f32(round_to_f32(1.0 / (1.0 + np.exp(-l32))) + b)
+        else:
+            key = round_to_f32(l32 + b)
+        if n_groups and n_groups > 0:
+            idx, kept_groups = select_group_limited(key, k, n_groups, topk_groups, key)
+        else:
+            idx = select_topk(key, k)
+    elif n_groups and n_groups > 0:
         s = 1.0 / (1.0 + np.exp(-l32)) if gate == GATE_SIGMOID_TOPK else l32
         idx, kept_groups = select_group_limited(l32, k, n_groups, topk_groups, s)
     else:
@@ -385,6 +404,58 @@ def combine(y_perm, pair_to_row: np.ndarray, topk_gate, T: int, k: int) -> np.nd
         kept = rows >= 0
         y[kept] += g[kept, j][:, None] * yp[rows[kept]]
     return y
+
+
+def router_probabilities(l: np.ndarray, gate: int) -> np.ndarray:
+    """Router probability of every expert for every token (all E, before top-k).
+
+    Softmax over the E logits for softmax gates; the sigmoid scores
+    normalised over all E for sigmoid gates (READING: the pages define P_i
+    only as the router probability allocated to expert i).
+    """
+    l = np.asarray(l, dtype=np.float64)
+    if gate == GATE_SIGMOID_TOPK:
+        s = 1.0 / (1.0 + np.exp(-l))
+        return s / s.sum(axis=1, keepdims=True)
+    m = l.max(axis=1, keepdims=True)
+    w = np.exp(l - m)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+def load_balance_stats(expert_counts: np.ndarray, probs: np.ndarray, k: int, alpha: float) -> Dict[str, object]:
+    """Auxiliary load-balancing loss L_aux = alpha * E * sum_i f_i * P_i.
+
+    [EPLLM] "Static Capacity Factors and Token Dropping", auxiliary-loss
+    equation: f_i the fraction of tokens dispatched to expert i, P_i the
+    router probability allocated to expert i. READING: f_i = c_i / (T*k)
+    (the share of (token, expert) pairs, before any capacity cut) and
+    P_i = mean over tokens of router_probabilities. Also returns the
+    imbalance max_i c_i / mean_i c_i ([EPA2A] "When it breaks": one expert
+    with several times its share stalls the layer).
+    """
+    c = np.asarray(expert_counts, dtype=np.float64)
+    p = np.asarray(probs, dtype=np.float64)
+    T, E = p.shape
+    f = c / (T * k)
+    P = p.mean(axis=0)
+    return {"f": f, "P": P, "aux_loss": float(alpha * E * np.sum(f * P)),
+            "imbalance": float(c.max() / c.mean()) if c.mean() > 0 else 0.0}
+
+
+def update_select_bias(select_bias: np.ndarray, expert_counts: np.ndarray, gamma: float) -> np.ndarray:
+    """One aux-loss-free balancing step: b_i <- b_i + gamma * sign(mean load - load_i).
+
+    [CH10] section 4 (aux-loss-free balancing by bias adjustment); [EPLLM]
+    "Modern Dropless Dynamic Dispatch" (dynamically adjusted bias terms on
+    routing scores). READING: the sign rule with step gamma (the page names
+    the mechanism, not the rule), in float32 like the bias itself.
+    """
+    b = np.asarray(select_bias, dtype=np.float32)
+    c = np.asarray(expert_counts, dtype=np.int64)
+    E = c.shape[0]
+    # sign(mean - c_i) compared in integers: mean*E = sum(c)
+    d = np.sign(c.sum() - E * c).astype(np.float32)
+    return (b + np.float32(gamma) * d).astype(np.float32)
 
 
 # ----------------------------------------------------------------------------------------------
