@@ -193,6 +193,31 @@ def main(argv=None):
     log(f"[bench] permute {permute_gbs:.0f} GB/s, combine {combine_gbs:.0f} GB/s, "
         f"FFN {ffn_tflops:.0f} TFLOP/s ({ffn_tflops / peak * 100:.1f}% of peak)")
 
+    # Stages beyond the forward step, timed on their own after it (not part of `value`):
+    # load balancing = the router with a selection-only bias and probability sums, then the
+    # statistics / bias-step kernel.
+    def time_calls(fn, reps=20):
+        fn()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        z.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / reps
+
+    sb = W.make_select_bias(cfg, dev)
+    part = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_ROUTE_STATS) // 4, dtype=torch.float32, device=dev)
+    stats = torch.empty(2 * cfg.E + 2, dtype=torch.float32, device=dev)
+    extra_ms = {
+        "route_ex": time_calls(lambda: M.moe_route_ex(d, inp["x"], inp["w_gate"], inp["bias"], sb, buf.topk_idx,
+                                                      buf.topk_gate, None, part, stream)),
+        "load_balance": time_calls(lambda: M.moe_load_balance(d, buf.expert_counts, part, 0.01, stats, 0.0, None,
+                                                              stream)),
+    }
+    for s_, v in extra_ms.items():
+        log(f"[bench]   {s_:12s} {v * 1e3:9.1f} us (outside the step)")
+
     cpu = None
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(cfg.name, 8)
@@ -210,6 +235,7 @@ def main(argv=None):
                    "ep_size_emulated": cfg.ep_size, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
                    "kept_rows": N, "parallelism": "1 GPU"},
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "extra_stage_ms": {s: round(v, 4) for s, v in extra_ms.items()},
         "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
         "gemm_mfma_frac": round(ffn_tflops / peak, 4),
         "roofline": roofline,

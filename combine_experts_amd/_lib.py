@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
-MOE_STAGE_LAYOUT, MOE_STAGE_FFN = 0, 1
+MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS = 0, 1, 2
 
 
 class MoEError(RuntimeError):
@@ -43,6 +43,8 @@ _SIG = {
     "moe_capacity": (ctypes.c_int, [ctypes.POINTER(moe_dims), _I32P]),
     "moe_workspace_size": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_route_ex": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_load_balance": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, ctypes.c_float, _P, ctypes.c_float, _P, _P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
@@ -148,6 +150,31 @@ def moe_route(d: moe_dims, x, w_gate, bias, topk_idx, topk_gate, logits=None, st
         _ptr(topk_idx, "topk_idx", torch.int32, d.T * d.top_k), _ptr(topk_gate, "topk_gate", torch.float32, d.T * d.top_k),
         _ptr(logits, "logits", torch.float32, d.T * d.E, nullable=True), _stream(stream))
     _check("moe_route", st)
+
+
+def moe_route_ex(d: moe_dims, x, w_gate, bias, select_bias, topk_idx, topk_gate, logits=None, prob_partials=None,
+                 stream=None) -> None:
+    dt = _elem_dtype(d)
+    n_part = (d.T + 63) // 64
+    st = load_library().moe_route_ex(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D), _ptr(w_gate, "w_gate", dt, d.E * d.D),
+        _ptr(bias, "bias", torch.float32, d.E, nullable=True),
+        _ptr(select_bias, "select_bias", torch.float32, d.E, nullable=True),
+        _ptr(topk_idx, "topk_idx", torch.int32, d.T * d.top_k), _ptr(topk_gate, "topk_gate", torch.float32, d.T * d.top_k),
+        _ptr(logits, "logits", torch.float32, d.T * d.E, nullable=True),
+        _ptr(prob_partials, "prob_partials", torch.float32, n_part * d.E, nullable=True), _stream(stream))
+    _check("moe_route_ex", st)
+
+
+def moe_load_balance(d: moe_dims, expert_counts, prob_partials, alpha: float, stats, gamma: float = 0.0,
+                     select_bias=None, stream=None) -> None:
+    n_part = (d.T + 63) // 64
+    st = load_library().moe_load_balance(
+        ctypes.byref(d), _ptr(expert_counts, "expert_counts", torch.int32, d.E),
+        _ptr(prob_partials, "prob_partials", torch.float32, n_part * d.E, nullable=d.T == 0), float(alpha),
+        _ptr(stats, "stats", torch.float32, 2 * d.E + 2), float(gamma),
+        _ptr(select_bias, "select_bias", torch.float32, d.E, nullable=True), _stream(stream))
+    _check("moe_load_balance", st)
 
 
 def moe_dispatch_layout(d: moe_dims, topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 100;
+constexpr int kAbiVersion = 101;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -57,6 +57,10 @@ int ffn_shape_ok(const moe_dims* d) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+size_t route_partial_rows(const moe_dims* d) {
+  return ((size_t)d->T + moe::kRouteTokPerBlock - 1) / moe::kRouteTokPerBlock;
+}
+
 }  // namespace
 
 extern "C" {
@@ -90,26 +94,49 @@ int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes) {
     *bytes = moe::layout_ws_bytes(d->T * d->top_k, d->E);
   } else if (stage == MOE_STAGE_FFN) {
     *bytes = ffn_ws_bytes(d);
+  } else if (stage == MOE_STAGE_ROUTE_STATS) {
+    *bytes = route_partial_rows(d) * (size_t)d->E * sizeof(float);
   } else {
     return MOE_ERR_INVALID_ARG;
   }
   return MOE_OK;
 }
 
-int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias, int32_t* topk_idx,
-              float* topk_gate, float* logits, hipStream_t stream) {
+int moe_route_ex(const moe_dims* d, const void* x, const void* w_gate, const float* bias, const float* select_bias,
+                 int32_t* topk_idx, float* topk_gate, float* logits, float* prob_partials, hipStream_t stream) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (d->T == 0) return MOE_OK;  // nothing to route
   if (x == nullptr || w_gate == nullptr || topk_idx == nullptr || topk_gate == nullptr) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_gate) || !aligned4(topk_idx) || !aligned4(topk_gate)) return MOE_ERR_INVALID_ARG;
   if ((bias && !aligned4(bias)) || (logits && !aligned4(logits))) return MOE_ERR_INVALID_ARG;
+  if ((select_bias && !aligned4(select_bias)) || (prob_partials && !aligned4(prob_partials)))
+    return MOE_ERR_INVALID_ARG;
   if (d->E > 256 || d->top_k > 32 || d->D % 8 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->dtype == MOE_BF16 && d->D % 64 != 0) return MOE_ERR_UNSUPPORTED;
   if (d->n_groups > 64 || (d->n_groups > 0 && d->top_k / d->topk_groups > 8)) return MOE_ERR_UNSUPPORTED;
-  moe::RouteArgs a{x, w_gate, bias, topk_idx, topk_gate, logits, d->T, d->D, d->E, d->top_k,
-                   d->n_groups, d->n_groups > 0 ? d->topk_groups : 0, d->gate};
+  moe::RouteArgs a{x, w_gate, bias, select_bias, topk_idx, topk_gate, logits, prob_partials, d->T, d->D, d->E,
+                   d->top_k, d->n_groups, d->n_groups > 0 ? d->topk_groups : 0, d->gate};
   return hip_status(moe::launch_route(a, d->dtype, stream));
+}
+
+int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias, int32_t* topk_idx,
+              float* topk_gate, float* logits, hipStream_t stream) {
+  return moe_route_ex(d, x, w_gate, bias, nullptr, topk_idx, topk_gate, logits, nullptr, stream);
+}
+
+int moe_load_balance(const moe_dims* d, const int32_t* expert_counts, const float* prob_partials, float alpha,
+                     float* stats, float gamma, float* select_bias, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (expert_counts == nullptr || stats == nullptr) return MOE_ERR_INVALID_ARG;
+  if (prob_partials == nullptr && d->T > 0) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(expert_counts) || !aligned4(stats) || (prob_partials && !aligned4(prob_partials)) ||
+      (select_bias && !aligned4(select_bias)))
+    return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(alpha) || !std::isfinite(gamma)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_load_balance(expert_counts, prob_partials, (int32_t)route_partial_rows(d), d->T, d->E,
+                                             d->top_k, alpha, stats, gamma, select_bias, stream));
 }
 
 int moe_dispatch_layout(const moe_dims* d, const int32_t* topk_idx, int32_t* expert_counts, int32_t* expert_offsets,

@@ -55,12 +55,18 @@ struct RouteArgs {
   const void* x;
   const void* w_gate;
   const float* bias;
+  const float* select_bias;   // selection-only bias [E] or null
   int32_t* topk_idx;
   float* topk_gate;
-  float* logits;
+  float* logits;              // [T,E] or null
+  float* prob_partials;       // [ceil(T/64), E] per-block router-probability sums, or null
   int32_t T, D, E, k, n_groups, topk_groups, gate;
 };
+constexpr int kRouteTokPerBlock = 64;
 hipError_t launch_route(const RouteArgs& a, int dtype, hipStream_t s);
+hipError_t launch_load_balance(const int32_t* expert_counts, const float* prob_partials, int32_t n_partials,
+                               int32_t T, int32_t E, int32_t k, float alpha, float* stats, float gamma,
+                               float* select_bias, hipStream_t s);
 
 hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_perm, int32_t T, int32_t D,
                           int32_t k, int dtype, hipStream_t s);

@@ -22,7 +22,7 @@
 namespace moe {
 namespace {
 
-constexpr int kTokPerBlock = 64;
+constexpr int kTokPerBlock = kRouteTokPerBlock;
 constexpr int kTokPerWave = 16;
 constexpr int kKC = 64;           // K slice per pipeline stage (two MFMA k-steps of 32)
 constexpr int kMaxE = 256;
@@ -44,7 +44,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 constexpr int kDepth = 4;
 
 template <int NT>  // 16-expert MFMA column tiles; experts padded to NT*16
-__device__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* bias,
+__device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* bias,
                             float* lds_logits, char* lds_raw, int T, int D, int E, int t0) {
   constexpr int epad = NT * 16;
   constexpr int STAGE = epad * (kKC / 8);        // 16-byte chunks per slice
@@ -129,7 +129,7 @@ __device__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restri
 }
 
 // ---- logits, fp32 FMA ------------------------------------------------------------------------------
-__device__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wg, const float* bias,
+__device__ __forceinline__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wg, const float* bias,
                            float* lds_logits, int epad, int T, int D, int E, int t0) {
   const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
   for (int i = 0; i < kTokPerWave; ++i) {
@@ -162,17 +162,48 @@ __device__ __forceinline__ bool better(float v, int e, float ov, int oe) {
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.f / (1.f + expf(-v)); }
 
 // ---- selection and gates for one token ------------------------------------------------------------
-__device__ void select_token(const float* lrow, int E, int k, int n_groups, int topk_groups, int gate,
+// Selection score under a selection-only bias: the sigmoid score under sigmoid gating, else the
+// logit, plus the expert's bias. Without a bias the selection ranks the logits themselves.
+__device__ __forceinline__ float sel_key(float v, float b, int gate) {
+  return ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v) : v) + b;
+}
+
+// Router probability numerators of one token: exp(l - max) for softmax gates, sigmoid(l) for
+// sigmoid gates; the caller divides by their sum over all E experts.
+__device__ __forceinline__ float prob_num(float v, float m, int gate) {
+  return (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v) : expf(v - m);
+}
+
+__device__ __forceinline__ void select_token(const float* lrow, int E, int k, int n_groups, int topk_groups, int gate,
+                             const float* __restrict__ sbias, float (&pacc)[kMaxPerLane], bool want_p,
                              int32_t* out_idx, float* out_gate) {
   const int lane = lane_id();
   const int n_per = (E + MOE_WAVE - 1) / MOE_WAVE;
-  float v[kMaxPerLane];
+  float v[kMaxPerLane], key[kMaxPerLane];
   bool ok[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = lane + i * MOE_WAVE;
     ok[i] = (i < n_per) && (e < E);
     v[i] = ok[i] ? lrow[e] : -INFINITY;
+    key[i] = (ok[i] && sbias != nullptr) ? sel_key(v[i], sbias[e], gate) : v[i];
+  }
+  if (want_p) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) m = fmaxf(m, v[i]);
+#pragma unroll
+    for (int off = MOE_WAVE / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, MOE_WAVE));
+    float num[kMaxPerLane], z = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) {
+      num[i] = ok[i] ? prob_num(v[i], m, gate) : 0.f;
+      z += num[i];
+    }
+#pragma unroll
+    for (int off = MOE_WAVE / 2; off >= 1; off >>= 1) z += __shfl_xor(z, off, MOE_WAVE);
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) pacc[i] += num[i] / z;
   }
   if (n_groups > 0) {
     const int gsize = E / n_groups;
@@ -185,7 +216,7 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
 #pragma unroll
       for (int i = 0; i < kMaxPerLane; ++i) {
         if (i >= n_per) break;
-        float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i];
+        float sv = (sbias != nullptr) ? key[i] : ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i]);
         float sum = 0.f;
         for (int rnd = 0; rnd < per; ++rnd) {
           float m = sv;
@@ -216,8 +247,10 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
 #pragma unroll
       for (int j = 0; j < 8; ++j) best[j] = -INFINITY;
       for (int m = 0; m < gsize; ++m) {
-        const float lv = lrow[lane * gsize + m];
-        float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(lv) : lv;
+        const int e = lane * gsize + m;
+        const float lv = lrow[e];
+        float sv = (sbias != nullptr) ? sel_key(lv, sbias[e], gate)
+                                      : ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(lv) : lv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           if (j < per && sv > best[j]) {
@@ -256,8 +289,8 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
       const int e = lane + i * MOE_WAVE;
-      if (ok[i] && better(bv, be, v[i], e)) {
-        bv = v[i];
+      if (ok[i] && better(bv, be, key[i], e)) {
+        bv = key[i];
         be = e;
       }
     }
@@ -278,8 +311,11 @@ __device__ void select_token(const float* lrow, int E, int k, int n_groups, int 
       my_e = be;
     }
   }
-  // gates
-  const float v0 = __shfl(my_v, 0, MOE_WAVE);
+  // gates, from the logits of the chosen experts (a selection bias never enters them)
+  if (sbias != nullptr) my_v = lrow[lane < k ? my_e : 0];
+  float v0 = __shfl(my_v, 0, MOE_WAVE);
+  if (sbias != nullptr)  // slot 0 need not hold the largest chosen logit any more
+    for (int j = 1; j < k; ++j) v0 = fmaxf(v0, __shfl(my_v, j, MOE_WAVE));
   float w = 0.f;
   if (lane < k) {
     if (gate == MOE_GATE_SIGMOID_TOPK) w = sigmoidf_(my_v);
@@ -325,19 +361,41 @@ __device__ bool fast_select_ok(int E, int k, int n_groups) {
 }
 
 template <int NT>
-__device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int k, int n_groups, int topk_groups,
-                        int gate, int32_t* out_idx, float* out_gate) {
+__device__ __forceinline__ void select4(const float* lds_logits, int trow0, int ntok, int E, int k, int n_groups, int topk_groups,
+                        int gate, bool has_sb, const float (&sb)[NT], float (&pacc)[NT], bool want_p,
+                        int32_t* out_idx, float* out_gate) {
   constexpr int epad = NT * 16;
   const int lane = lane_id();
   const int seg = lane / 16, L = lane % 16;
   const bool tok_ok = seg < ntok;
-  const float* lrow = lds_logits + (trow0 + (tok_ok ? seg : 0)) * epad + L * NT;
-  float v[NT];
+  const float* ltok = lds_logits + (trow0 + (tok_ok ? seg : 0)) * epad;
+  const float* lrow = ltok + L * NT;
+  float v[NT], key[NT];
   bool ok[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     v[i] = lrow[i];
+    key[i] = has_sb ? sel_key(v[i], sb[i], gate) : v[i];
     ok[i] = true;
+  }
+  if (want_p) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) m = fmaxf(m, v[i]);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, MOE_WAVE));
+    float num[NT], z = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      num[i] = prob_num(v[i], m, gate);
+      z += num[i];
+    }
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) z += __shfl_xor(z, off, MOE_WAVE);
+    if (tok_ok) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i) pacc[i] += num[i] / z;
+    }
   }
   if (n_groups > 0) {
     const int gsize = E / n_groups;
@@ -349,7 +407,7 @@ __device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int
     for (int j = 0; j < 8; ++j) best[j] = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      float sv = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i];
+      float sv = has_sb ? key[i] : ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j < per && sv > best[j]) {
@@ -406,8 +464,8 @@ __device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
       const int e = L * NT + i;
-      if (ok[i] && better(bv, be, v[i], e)) {
-        bv = v[i];
+      if (ok[i] && better(bv, be, key[i], e)) {
+        bv = key[i];
         be = e;
       }
     }
@@ -428,7 +486,10 @@ __device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int
       my_e = be;
     }
   }
-  const float v0 = __shfl(my_v, seg * 16, MOE_WAVE);
+  if (has_sb) my_v = ltok[L < k ? my_e : 0];  // gates use the chosen experts' logits
+  float v0 = __shfl(my_v, seg * 16, MOE_WAVE);
+  if (has_sb)
+    for (int j = 1; j < k; ++j) v0 = fmaxf(v0, __shfl(my_v, seg * 16 + j, MOE_WAVE));
   float w = 0.f, denom = 0.f;
   if (gate == MOE_GATE_SOFTMAX_FULL) {
     float m = -INFINITY;
@@ -453,12 +514,16 @@ __device__ void select4(const float* lds_logits, int trow0, int ntok, int E, int
   }
 }
 
-template <typename T, int NT>
+// BAL = false is the plain router: the selection bias and the probability sums are compiled out.
+template <typename T, int NT, bool BAL>
 __global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, const T* __restrict__ wg,
-                                                    const float* __restrict__ bias, int32_t* __restrict__ topk_idx,
-                                                    float* __restrict__ topk_gate, float* __restrict__ logits,
+                                                    const float* __restrict__ bias, const float* __restrict__ sbias_,
+                                                    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                                                    float* __restrict__ logits, float* __restrict__ prob_partials_,
                                                     int T_, int D, int E, int k, int n_groups, int topk_groups,
                                                     int gate) {
+  const float* sbias = BAL ? sbias_ : nullptr;
+  float* prob_partials = BAL ? prob_partials_ : nullptr;
   constexpr int epad = NT * 16;
   extern __shared__ __attribute__((aligned(16))) char lds_raw[];
   float* lds_logits = reinterpret_cast<float*>(lds_raw);
@@ -478,46 +543,87 @@ __global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, con
       for (int e = lane; e < E; e += MOE_WAVE) logits[(size_t)tok * E + e] = lds_logits[trow * epad + e];
     }
   }
+  const bool want_p = prob_partials != nullptr;
+  // per-wave sums of router probabilities, one row of epad floats per wave, after the logit tile
+  float* wsum = lds_logits + kTokPerBlock * epad;
   if (fast_select_ok<NT>(E, k, n_groups)) {
+    const int L = lane % 16;
+    float sb[NT], pacc[NT];
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      sb[i] = sbias != nullptr ? sbias[L * NT + i] : 0.f;
+      pacc[i] = 0.f;
+    }
     for (int i = 0; i < kTokPerWave; i += 4) {
       const int trow = wave * kTokPerWave + i;
       const int tok = t0 + trow;
       if (tok >= T_) break;
-      select4<NT>(lds_logits, trow, min(4, T_ - tok), E, k, n_groups, topk_groups, gate, topk_idx + (size_t)tok * k,
-                  topk_gate + (size_t)tok * k);
+      select4<NT>(lds_logits, trow, min(4, T_ - tok), E, k, n_groups, topk_groups, gate, sbias != nullptr, sb, pacc,
+                  want_p, topk_idx + (size_t)tok * k, topk_gate + (size_t)tok * k);
+    }
+    if (want_p) {
+      // fold the four token segments: lane L of segment 0 ends with the wave's sums for its experts
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        pacc[i] += __shfl_xor(pacc[i], 16, MOE_WAVE);
+        pacc[i] += __shfl_xor(pacc[i], 32, MOE_WAVE);
+      }
+      if (lane < 16)
+#pragma unroll
+        for (int i = 0; i < NT; ++i) wsum[wave * epad + L * NT + i] = pacc[i];
     }
   } else {
+    float pacc[kMaxPerLane] = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < kTokPerWave; ++i) {
       const int trow = wave * kTokPerWave + i;
       const int tok = t0 + trow;
       if (tok >= T_) break;
-      select_token(lds_logits + trow * epad, E, k, n_groups, topk_groups, gate, topk_idx + (size_t)tok * k,
-                   topk_gate + (size_t)tok * k);
+      select_token(lds_logits + trow * epad, E, k, n_groups, topk_groups, gate, sbias, pacc, want_p,
+                   topk_idx + (size_t)tok * k, topk_gate + (size_t)tok * k);
     }
+    if (want_p)
+#pragma unroll
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (lane + i * MOE_WAVE < epad) wsum[wave * epad + lane + i * MOE_WAVE] = pacc[i];
+  }
+  if (want_p) {
+    // block partial, waves summed in a fixed order: the result does not depend on scheduling
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      prob_partials[(size_t)blockIdx.x * E + e] =
+          ((wsum[e] + wsum[epad + e]) + wsum[2 * epad + e]) + wsum[3 * epad + e];
   }
 }
 
-template <int NT>
+template <int NT, bool BAL>
 hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
   constexpr int epad = NT * 16;
   const int blocks = (a.T + kTokPerBlock - 1) / kTokPerBlock;
-  const size_t lds_logits = (size_t)kTokPerBlock * epad * sizeof(float);
+  // logit tile [64 x epad] plus four per-wave probability rows
+  const size_t lds_logits = (size_t)(kTokPerBlock + 4) * epad * sizeof(float);
   if (dtype == MOE_BF16) {
     const size_t lds_w = (size_t)kDepth * epad * kKC * sizeof(bf16_t);
     const size_t lds = lds_w > lds_logits ? lds_w : lds_logits;
     // dynamic LDS above the default 64 KB needs the per-kernel limit raised (once per process)
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<bf16_t, NT>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&route_kernel<bf16_t, NT, BAL>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)lds);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((route_kernel<bf16_t, NT>), dim3(blocks), dim3(256), lds, s, (const bf16_t*)a.x,
-                       (const bf16_t*)a.w_gate, a.bias, a.topk_idx, a.topk_gate, a.logits, a.T, a.D, a.E, a.k,
-                       a.n_groups, a.topk_groups, a.gate);
+    hipLaunchKernelGGL((route_kernel<bf16_t, NT, BAL>), dim3(blocks), dim3(256), lds, s, (const bf16_t*)a.x,
+                       (const bf16_t*)a.w_gate, a.bias, a.select_bias, a.topk_idx, a.topk_gate, a.logits,
+                       a.prob_partials, a.T, a.D, a.E, a.k, a.n_groups, a.topk_groups, a.gate);
   } else {
-    hipLaunchKernelGGL((route_kernel<float, NT>), dim3(blocks), dim3(256), lds_logits, s, (const float*)a.x,
-                       (const float*)a.w_gate, a.bias, a.topk_idx, a.topk_gate, a.logits, a.T, a.D, a.E, a.k,
-                       a.n_groups, a.topk_groups, a.gate);
+    hipLaunchKernelGGL((route_kernel<float, NT, BAL>), dim3(blocks), dim3(256), lds_logits, s, (const float*)a.x,
+                       (const float*)a.w_gate, a.bias, a.select_bias, a.topk_idx, a.topk_gate, a.logits,
+                       a.prob_partials, a.T, a.D, a.E, a.k, a.n_groups, a.topk_groups, a.gate);
   }
   return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
+  if (a.select_bias != nullptr || a.prob_partials != nullptr) return launch_route_nt<NT, true>(a, dtype, s);
+  return launch_route_nt<NT, false>(a, dtype, s);
 }
 
 }  // namespace

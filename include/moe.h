@@ -14,6 +14,7 @@
  *   [EPA2A] "Expert Parallelism and All-to-All"
  *   [A2AC]  "Expert Parallelism > All-to-All Communication"
  *   [COMM]  "Expert Parallelism > Communication Overhead Analysis"
+ *   [CH10]  "Chapter 10: MoE parallelism" (infra-guide), section 4 on load balancing
  *   [EPLLM] "Expert Parallelism in Large Language Models: How All-to-All Token Dispatch, Capacity
  *           Factors, and Parallel Folding Scale MoE Architectures"
  *
@@ -65,7 +66,11 @@ enum moe_act {
 
 enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 
-enum moe_stage { MOE_STAGE_LAYOUT = 0, MOE_STAGE_FFN = 1 };
+enum moe_stage {
+  MOE_STAGE_LAYOUT = 0,     /* scratch of moe_dispatch_layout */
+  MOE_STAGE_FFN = 1,        /* scratch of moe_expert_ffn */
+  MOE_STAGE_ROUTE_STATS = 2 /* the prob_partials buffer of moe_route_ex / moe_load_balance */
+};
 
 /* Problem statement of one layer call ([COMM] volume equation: B*S tokens as T, top-k as K,
  * hidden size D; [EPLLM] capacity equation; [A2AC] expert -> device map).
@@ -105,6 +110,36 @@ int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes);
  * for MOE_BF16 D % 64 != 0. */
 int moe_route(const moe_dims* d, const void* x, const void* w_gate, const float* bias,
               int32_t* topk_idx, float* topk_gate, float* logits, hipStream_t stream);
+
+/* Router with the two load-balancing by-products (moe_route is this call with both NULL).
+ *   select_bias [E] float32 or NULL: a per-expert bias that moves the selection only -- the
+ *     bias-adjusted routing scores of aux-loss-free balancing ([EPLLM] "Modern Dropless Dynamic
+ *     Dispatch"; [CH10] section 4, load balancing). The selection ranks s_e + select_bias[e], where
+ *     s_e = sigmoid(logit_e) under MOE_GATE_SIGMOID_TOPK and s_e = logit_e otherwise, in float32,
+ *     ties to the lower index; with a group limit the group scores are taken on these biased
+ *     scores. Gate values are computed from the unbiased logits of the chosen experts.
+ *   prob_partials [ceil(T/64), E] float32 out, or NULL: row b holds, for each expert, the sum of
+ *     the router probabilities of tokens [64b, 64b+64) -- softmax over all E logits for softmax
+ *     gates, sigmoid scores normalised over all E for sigmoid gates. Its size in bytes is
+ *     moe_workspace_size(MOE_STAGE_ROUTE_STATS); moe_load_balance consumes it.
+ * Everything else as moe_route. */
+int moe_route_ex(const moe_dims* d, const void* x, const void* w_gate, const float* bias,
+                 const float* select_bias, int32_t* topk_idx, float* topk_gate, float* logits,
+                 float* prob_partials, hipStream_t stream);
+
+/* Load-balance statistics of one routed batch ([EPLLM] "Static Capacity Factors and Token
+ * Dropping", auxiliary-loss equation L_aux = alpha * E * sum_i f_i * P_i) and, optionally, one
+ * aux-loss-free bias step.
+ *   expert_counts [E] int32 in (moe_dispatch_layout's, before any capacity cut);
+ *   prob_partials in (moe_route_ex's; may be NULL only when T == 0);
+ *   stats [2E+2] float32 out: f_i = counts_i / (T*top_k) for i < E; P_i = mean router probability
+ *     of expert i at E+i; L_aux at 2E; the load imbalance max_i counts_i / mean_i counts_i at 2E+1
+ *     ([EPA2A] "When it breaks": the busiest expert sets the pace). All zero when T == 0.
+ *   select_bias [E] float32 in/out, or NULL: b_i += gamma * sign(mean load - load_i), the sign
+ *     decided exactly in integers, the add in float32.
+ * Deterministic: every sum runs in a fixed order. One small kernel (one workgroup). */
+int moe_load_balance(const moe_dims* d, const int32_t* expert_counts, const float* prob_partials,
+                     float alpha, float* stats, float gamma, float* select_bias, hipStream_t stream);
 
 /* Dispatch layout ([EPA2A] "The two exchanges": each device sorts its tokens by destination
  * expert; [EPLLM] pipeline steps 1-2: replicate each token k times tagged with expert and rank,

@@ -22,7 +22,7 @@ __all__ = [
     "group_scores", "gate_weights", "route", "decisive_tokens", "capacity", "dispatch_layout",
     "send_counts", "dispatch_matrix", "permute", "silu", "gelu", "expert_ffn", "expert_ffn_rows",
     "combine", "comm_volume_elements", "dispatch_volume_bytes", "layer_forward",
-    "router_probabilities", "load_balance_stats", "update_select_bias",
+    "router_probabilities", "load_balance_stats", "update_select_bias", "selection_key",
 ]
 
 GATE_SOFTMAX_TOPK = 0
@@ -148,6 +148,19 @@ def gate_weights(l: np.ndarray, topk_idx: np.ndarray, mode: int) -> np.ndarray:
     raise ValueError(f"unknown gate mode {mode}")
 
 
+def selection_key(l32: np.ndarray, gate: int, select_bias) -> np.ndarray:
+    """Score that a selection-only bias ranks by: (sigmoid(l) under sigmoid gating, else l) + b.
+
+    READING of the bias-adjusted routing scores ([CH10] section 4; [EPLLM]
+    "Modern Dropless Dynamic Dispatch"): each term is rounded to float32 as
+    the kernel holds it.
+    """
+    b = np.asarray(as_f64(select_bias), dtype=np.float64)[None, :]
+    if gate == GATE_SIGMOID_TOPK:
+        return round_to_f32(round_to_f32(1.0 / (1.0 + np.exp(-np.asarray(l32, dtype=np.float64)))) + b)
+    return round_to_f32(np.asarray(l32, dtype=np.float64) + b)
+
+
 def route(x, w_gate, bias, k: int, gate: int, n_groups: int = 0, topk_groups: int = 0,
           select_bias=None) -> Dict[str, np.ndarray]:
     """Router step end to end: logits, selection, gates.
@@ -167,11 +180,7 @@ def route(x, w_gate, bias, k: int, gate: int, n_groups: int = 0, topk_groups: in
     l32 = round_to_f32(l64)
     kept_groups = None
     if select_bias is not None:
-        b = np.asarray(as_f64(select_bias), dtype=np.float64)[None, :]
-        if gate == GATE_SIGMOID_TOPK:
-            key = round_to_f32(round_to_f32(1.0 / (1.0 + np.exp(-l32))) + b)
-        else:
-            key = round_to_f32(l32 + b)
+        key = selection_key(l32, gate, select_bias)
         if n_groups and n_groups > 0:
             idx, kept_groups = select_group_limited(key, k, n_groups, topk_groups, key)
         else:

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 100
+    assert M.moe_abi_version() == 101
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -58,6 +58,9 @@ def test_workspace_sizes():
     d = M.make_dims(16384, 7168, 256, 8, 2048)
     assert M.moe_workspace_size(d, M.MOE_STAGE_FFN) >= 16384 * 8 * 2048 * 2
     assert M.moe_workspace_size(d, M.MOE_STAGE_LAYOUT) >= 256 * 4
+    # one row of E float32 router-probability sums per 64-token router block
+    assert M.moe_workspace_size(d, M.MOE_STAGE_ROUTE_STATS) == 256 * 256 * 4
+    assert M.moe_workspace_size(M.make_dims(65, 64, 8, 2, 64), M.MOE_STAGE_ROUTE_STATS) == 2 * 8 * 4
     with pytest.raises(M.MoEError) as ei:
         M.moe_workspace_size(d, 7)
     assert ei.value.status == M.MOE_ERR_INVALID_ARG
@@ -129,3 +132,33 @@ def test_product_path_does_not_import_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
+
+
+def test_load_balance_host_checks():
+    lib = M.load_library()
+    d = M.make_dims(16, 64, 8, 2, 64)
+    fake = ctypes.c_void_p(256)
+    # counts and stats are required; partials are required when T > 0
+    assert lib.moe_load_balance(ctypes.byref(d), None, fake, 0.01, fake, 0.0, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_balance(ctypes.byref(d), fake, None, 0.01, fake, 0.0, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_balance(ctypes.byref(d), fake, fake, 0.01, None, 0.0, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_balance(ctypes.byref(d), fake, fake, float("inf"), fake, 0.0, None, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert lib.moe_load_balance(ctypes.byref(d), ctypes.c_void_p(258), fake, 0.01, fake, 0.0, None, None) == \
+        M.MOE_ERR_INVALID_ARG
+
+
+def test_route_ex_host_checks():
+    lib = M.load_library()
+    d = M.make_dims(16, 64, 8, 2, 64)
+    fake = ctypes.c_void_p(256)
+    mis = ctypes.c_void_p(258)
+    assert lib.moe_route_ex(ctypes.byref(d), None, fake, None, None, fake, fake, None, None, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_ex(ctypes.byref(d), fake, fake, None, mis, fake, fake, None, None, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_ex(ctypes.byref(d), fake, fake, None, None, fake, fake, None, mis, None) == \
+        M.MOE_ERR_INVALID_ARG
+    d = M.make_dims(16, 64, 300, 2, 64)
+    assert lib.moe_route_ex(ctypes.byref(d), fake, fake, None, fake, fake, fake, None, fake, None) == \
+        M.MOE_ERR_UNSUPPORTED

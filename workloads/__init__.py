@@ -162,6 +162,17 @@ def make_bias(cfg: MoEConfig, device="cpu") -> Optional[torch.Tensor]:
     raise ValueError(cfg.bias)
 
 
+def make_select_bias(cfg: MoEConfig, device="cpu", std: Optional[float] = None) -> torch.Tensor:
+    """A selection-only per-expert bias [E] float32, N(0, std^2).
+
+    Default std: 0.05 under sigmoid gating (the scores it is added to lie in (0, 1)), 0.5 on
+    logits otherwise -- large enough to move many selections, small enough to keep most.
+    """
+    if std is None:
+        std = 0.05 if cfg.gate == GATE_SIGMOID_TOPK else 0.5
+    return _normal((cfg.E,), std, torch.float32, device, cfg.seed, "select_bias")
+
+
 def make_expert_weights(cfg: MoEConfig, e: int, device="cpu"):
     """(W1[e] [F,D], W3[e] [F,D] or None, W2[e] [D,F]) for one expert."""
     dt = torch_dtype(cfg.dtype)
