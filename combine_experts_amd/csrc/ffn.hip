@@ -91,8 +91,8 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // ends up with 4 consecutive output columns of one token row: 8-byte stores in the epilogue.
 //
 // K runs in 64-deep stages through a 2-slot LDS ring (64 KB per slot). Loads go straight from
-// global memory into LDS (16 bytes per lane, no register staging) and are issued two per k-step,
-// one stage ahead. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
+// global memory into LDS (16 bytes per lane, no register staging); a whole stage is issued at once,
+// one stage ahead, at the start of the stage before it. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
 // ch ^ ((row >> 1) & 7), so the 32 rows one fragment read touches fall on distinct banks.
 //
 // Tile order: a block's tile comes from its index through an XCD-aware map (workgroups are handed
@@ -192,8 +192,12 @@ __device__ __forceinline__ int gbrow(int wn, int j) {
 
 template <int ACT>  // active 32-row blocks of this wave
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
-                                           const int (&aoff)[G_KS][4], const int (&boff)[G_KS][2], int wave, int nk) {
+                                           const int (&aoff)[G_KS][4], const int (&boff)[G_KS][2], int wave, int nk,
+                                           int mrows) {
+  // load i fills tile rows [i*64, i*64+64) of A (i < G_ACH/GTH) or a part of B; A loads wholly past
+  // the tile's rows are skipped (those rows feed only accumulators that are never stored)
   auto issue = [&](int kt, int buf, int i) {
+    if (i * GTH < G_ACH && i * (GTH / GKCH) >= mrows) return;
     __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * GBK),
                                      (__attribute__((address_space(3))) void*)(lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE),
                                      16, 0, 0);
@@ -217,10 +221,11 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, con
 #pragma unroll
     for (int ks = 0; ks < G_KS; ++ks) {
       const int c = ks & 1, n = c ^ 1;
-      // stage kt+1 goes to the other slot, free since the barrier that ended iteration kt-1
-      if (refill) {
-        issue(kt + 1, buf ^ 1, 2 * ks);
-        issue(kt + 1, buf ^ 1, 2 * ks + 1);
+      // all of stage kt+1 goes to the other slot at once, at the start of stage kt (the slot is free
+      // since the barrier that ended iteration kt-1): the loads get a whole stage to land
+      if (refill && ks == 0) {
+#pragma unroll
+        for (int i = 0; i < G_LPS; ++i) issue(kt + 1, buf ^ 1, i);
       }
       if (ks < G_KS - 1) {
         frag(buf, ks + 1, n);
@@ -305,10 +310,10 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
-    case 4: gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk); break;
-    case 3: gemm_kloop<3>(acc, lds, src, aoff, boff, wave, nk); break;
-    case 2: gemm_kloop<2>(acc, lds, src, aoff, boff, wave, nk); break;
-    default: gemm_kloop<1>(acc, lds, src, aoff, boff, wave, nk); break;
+    case 4: gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
+    case 3: gemm_kloop<3>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
+    case 2: gemm_kloop<2>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
+    default: gemm_kloop<1>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
 #pragma unroll
