@@ -23,6 +23,7 @@ __all__ = [
     "send_counts", "dispatch_matrix", "permute", "silu", "gelu", "expert_ffn", "expert_ffn_rows",
     "combine", "comm_volume_elements", "dispatch_volume_bytes", "layer_forward",
     "router_probabilities", "load_balance_stats", "update_select_bias", "selection_key",
+    "source_shards", "recv_layout", "cluster_forward", "padded_layout", "permute_padded",
 ]
 
 GATE_SOFTMAX_TOPK = 0
@@ -313,6 +314,137 @@ def dispatch_matrix(topk_idx_per_src: np.ndarray, E: int, n_dev: int) -> np.ndar
     out = np.zeros((n_dev, n_dev), dtype=np.int64)
     for src in range(n_dev):
         out[src] = send_counts(topk_idx_per_src[src], E, n_dev)
+    return out
+
+
+def source_shards(T: int, n_src: int):
+    """Token ranges of n_src equal source shards: shard s owns tokens [s*T/n_src, (s+1)*T/n_src).
+
+    READING of the routing simulation in [A2AC]: every device routes the same
+    number of local tokens; shards are contiguous.
+    """
+    if n_src < 1 or T % n_src != 0:
+        raise ValueError("T must split evenly over the source shards")
+    ts = T // n_src
+    return [(s * ts, (s + 1) * ts) for s in range(n_src)]
+
+
+def recv_layout(src_expert_offsets: np.ndarray, E: int, n_dst: int, r: int, src_stride: int) -> Dict[str, np.ndarray]:
+    """Receive side of destination rank r: which sent rows it gets and how it regroups them.
+
+    [EPA2A] "The two exchanges": after the dispatch exchange each device holds,
+    from every source, a chunk of rows sorted by its local experts; the grouped
+    GEMM wants all rows of one local expert together. [A2AC]: rank r owns
+    experts [r*E/n_dst, (r+1)*E/n_dst).
+
+    ``src_expert_offsets[s]`` is source s's own compact layout (expert offsets,
+    E+1 entries); source s's sent rows live at rows s*src_stride + j of one
+    concatenated send buffer. READING: the regrouped order is (local expert,
+    source, source row order).
+
+    Returns ``recv_counts[s]`` (rows s sends to r), ``expert_offsets`` [epr+1]
+    of the regrouped rows, and ``grouped_to_src_row`` [n]: the send-buffer row
+    of each regrouped row.
+    """
+    off = np.asarray(src_expert_offsets, dtype=np.int64)
+    n_src = off.shape[0]
+    epr = E // n_dst
+    lo, hi = r * epr, (r + 1) * epr
+    counts = off[:, lo + 1:hi + 1] - off[:, lo:hi]             # [n_src, epr]
+    recv_counts = counts.sum(axis=1)
+    exp_off = np.concatenate([[0], np.cumsum(counts.sum(axis=0))]).astype(np.int64)
+    rows = []
+    for el in range(epr):
+        for s in range(n_src):
+            start = s * src_stride + off[s, lo + el]
+            rows.extend(range(int(start), int(start + counts[s, el])))
+    return {"recv_counts": recv_counts, "expert_offsets": exp_off,
+            "grouped_to_src_row": np.asarray(rows, dtype=np.int64)}
+
+
+def cluster_forward(inputs: Dict, cfg, n_ep: int) -> Dict[str, object]:
+    """The layer on n_ep emulated devices: shard, route, send layout, exchange, regroup, FFN, return, combine.
+
+    [EPA2A] "The two exchanges" (dispatch then combine all-to-all around the
+    expert compute); [EPLLM] "The Execution Pipeline" steps 1-6; [A2AC]
+    (contiguous expert -> device map, per-device send counts). Dropless.
+    Every device routes its own shard; device r runs its E/n_ep experts on the
+    rows it receives, regrouped per local expert; the outputs travel back to
+    their source and are combined there. Returns y [T, D] and the [src, dst]
+    kept-row matrix.
+    """
+    T, E, k, D = cfg.T, cfg.E, cfg.top_k, cfg.D
+    x = as_f64(inputs["x"])
+    shards = source_shards(T, n_ep)
+    ts = T // n_ep
+    stride = ts * k
+    epr = E // n_ep
+    w1, w3, w2 = inputs["w1"], inputs.get("w3"), inputs["w2"]
+    send = np.zeros((n_ep * stride, D))
+    src_off = np.zeros((n_ep, E + 1), dtype=np.int64)
+    per_src = []
+    for s, (a, b) in enumerate(shards):
+        r_s = route(inputs["x"][a:b], inputs["w_gate"], inputs.get("bias"), k, cfg.gate, cfg.n_groups,
+                    cfg.topk_groups)
+        lay = dispatch_layout(r_s["topk_idx"], E, n_ep, None)
+        n = lay["n_kept"]
+        send[s * stride: s * stride + n] = permute(x[a:b], lay["row_to_pair"], k, n)
+        src_off[s] = lay["expert_offsets"]
+        per_src.append((r_s, lay))
+    back = np.zeros_like(send)
+    matrix = np.zeros((n_ep, n_ep), dtype=np.int64)
+    for r in range(n_ep):
+        rl = recv_layout(src_off, E, n_ep, r, stride)
+        matrix[:, r] = rl["recv_counts"]
+        g2s = rl["grouped_to_src_row"]
+        grouped = send[g2s]
+        w1r = w1[r * epr:(r + 1) * epr]
+        w3r = None if w3 is None else w3[r * epr:(r + 1) * epr]
+        w2r = w2[r * epr:(r + 1) * epr]
+        y_grouped = expert_ffn(grouped, rl["expert_offsets"], w1r, w3r, w2r, cfg.act)
+        back[g2s] = y_grouped
+    y = np.zeros((T, D))
+    for s, (a, b) in enumerate(shards):
+        r_s, lay = per_src[s]
+        y[a:b] = combine(back[s * stride:(s + 1) * stride], lay["pair_to_row"], r_s["topk_gate"], ts, k)
+    return {"y": y, "matrix": matrix, "src_expert_offsets": src_off}
+
+
+def padded_layout(topk_idx: np.ndarray, E: int, C: int) -> Dict[str, object]:
+    """GShard-style fixed-capacity layout: expert e owns slots [e*C, (e+1)*C) of an [E*C] buffer.
+
+    [EPLLM] "Static Capacity Factors and Token Dropping": each expert gets a
+    buffer of C = ceil(CF*k*T/E) rows; pairs past C are dropped and unused
+    slots are padding. Kept pairs are the same as in the compact layout with
+    the same C (first C pairs of each expert in pair-id order); pair p of
+    expert e with rank q < C goes to slot e*C + q.
+    Returns pair_to_slot [T*k] (-1 dropped), slot_to_pair [E*C] (-1 padding),
+    padded_offsets [E+1] = e*C, and the padding (empty slots) count.
+    """
+    flat = np.asarray(topk_idx, dtype=np.int64).reshape(-1)
+    P = flat.shape[0]
+    pair_to_slot = np.full(P, -1, dtype=np.int64)
+    slot_to_pair = np.full(E * C, -1, dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    for p in range(P):                      # pair-id order: rank within the expert
+        e = int(flat[p])
+        q = int(seen[e])
+        seen[e] += 1
+        if q < C:
+            pair_to_slot[p] = e * C + q
+            slot_to_pair[e * C + q] = p
+    return {"pair_to_slot": pair_to_slot, "slot_to_pair": slot_to_pair,
+            "padded_offsets": np.arange(E + 1, dtype=np.int64) * C,
+            "padding": int((slot_to_pair < 0).sum()), "n_kept": int((pair_to_slot >= 0).sum())}
+
+
+def permute_padded(x, slot_to_pair: np.ndarray, k: int) -> np.ndarray:
+    """x_pad[s] = x[slot_to_pair[s] // k] for filled slots, 0 for padding slots."""
+    xa = as_f64(x)
+    s2p = np.asarray(slot_to_pair, dtype=np.int64)
+    out = np.zeros((s2p.shape[0], xa.shape[1]))
+    filled = s2p >= 0
+    out[filled] = xa[s2p[filled] // k]
     return out
 
 
