@@ -7,7 +7,8 @@ built in-tree by ``python -m combine_experts_amd.build``.
 from ._lib import (  # noqa: F401
     MoEError, moe_dims, make_dims, dims_from_config, load_library, LIB_PATH,
     moe_abi_version, moe_status_str, moe_capacity, moe_workspace_size, moe_route, moe_route_ex,
-    moe_load_balance, moe_dispatch_layout,
+    moe_load_balance, moe_dispatch_layout, moe_dispatch_matrix, moe_recv_layout, moe_gather_rows, moe_scatter_rows,
+    moe_padded_layout, moe_permute_padded, moe_expert_ffn_padded_up, moe_expert_ffn_padded_down,
     moe_permute, moe_expert_ffn, moe_expert_ffn_up, moe_expert_ffn_down, moe_unpermute_combine,
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL, MOE_ACT_SWIGLU, MOE_ACT_GELU,

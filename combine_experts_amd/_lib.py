@@ -45,6 +45,15 @@ _SIG = {
     "moe_route": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_route_ex": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_load_balance": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, ctypes.c_float, _P, ctypes.c_float, _P, _P]),
+    "moe_dispatch_matrix": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, ctypes.c_int32, _P, _P]),
+    "moe_recv_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _P, _P,
+                                       _P, _P, ctypes.c_int32, _P]),
+    "moe_gather_rows": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.c_int64, _P, _P, _P, _P]),
+    "moe_scatter_rows": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.c_int64, _P, _P, _P, _P]),
+    "moe_padded_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P]),
+    "moe_permute_padded": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
+    "moe_expert_ffn_padded_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_padded_down": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
@@ -229,10 +238,107 @@ def moe_expert_ffn(d: moe_dims, x_perm, expert_offsets, w1, w3, w2, y_perm, ws, 
     _check("moe_expert_ffn", st)
 
 
-def moe_unpermute_combine(d: moe_dims, y_perm, pair_to_row, topk_gate, y, stream=None) -> None:
+def moe_unpermute_combine(d: moe_dims, y_perm, pair_to_row, topk_gate, y, stream=None, n_rows=None) -> None:
+    """n_rows: rows y_perm holds (default T*top_k; E*C for the padded buffer)."""
     dt = _elem_dtype(d)
     P = d.T * d.top_k
+    rows = P if n_rows is None else int(n_rows)
     st = load_library().moe_unpermute_combine(
-        ctypes.byref(d), _ptr(y_perm, "y_perm", dt, P * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        ctypes.byref(d), _ptr(y_perm, "y_perm", dt, rows * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
         _ptr(topk_gate, "topk_gate", torch.float32, P), _ptr(y, "y", dt, d.T * d.D), _stream(stream))
     _check("moe_unpermute_combine", st)
+
+
+# ---- cluster view and padded layout ----------------------------------------------------------------
+
+def moe_dispatch_matrix(d: moe_dims, topk_idx, n_src: int, matrix, stream=None) -> None:
+    st = load_library().moe_dispatch_matrix(
+        ctypes.byref(d), _ptr(topk_idx, "topk_idx", torch.int32, d.T * d.top_k, nullable=d.T == 0), int(n_src),
+        _ptr(matrix, "matrix", torch.int32, n_src * d.ep_size), _stream(stream))
+    _check("moe_dispatch_matrix", st)
+
+
+def moe_recv_layout(d: moe_dims, n_src: int, rank: int, src_stride: int, src_expert_offsets, recv_counts,
+                    expert_offsets, grouped_to_src_row, stream=None) -> None:
+    epr = d.E // d.ep_size
+    n_rows_max = 0 if grouped_to_src_row is None else grouped_to_src_row.numel()
+    i32 = torch.int32
+    st = load_library().moe_recv_layout(
+        ctypes.byref(d), int(n_src), int(rank), int(src_stride),
+        _ptr(src_expert_offsets, "src_expert_offsets", i32, n_src * (d.E + 1)),
+        _ptr(recv_counts, "recv_counts", i32, n_src), _ptr(expert_offsets, "expert_offsets", i32, epr + 1),
+        _ptr(grouped_to_src_row, "grouped_to_src_row", i32, nullable=True), n_rows_max, _stream(stream))
+    _check("moe_recv_layout", st)
+
+
+def _rows(t, name, d):
+    if t.numel() % d.D != 0:
+        raise ValueError(f"{name} must hold whole rows of {d.D} elements")
+    return t.numel() // d.D
+
+
+def moe_gather_rows(d: moe_dims, row_map, src, dst, stream=None) -> None:
+    """dst[i] = src[row_map[i]] for row_map[i] >= 0, i < row_map.numel(); rows of D elements."""
+    dt = _elem_dtype(d)
+    n = row_map.numel()
+    _ptr(src, "src", dt)
+    if _rows(dst, "dst", d) < n:
+        raise ValueError("dst has fewer rows than row_map")
+    st = load_library().moe_gather_rows(ctypes.byref(d), n, _ptr(row_map, "row_map", torch.int32), src.data_ptr(),
+                                        _ptr(dst, "dst", dt), _stream(stream))
+    _check("moe_gather_rows", st)
+
+
+def moe_scatter_rows(d: moe_dims, row_map, src, dst, stream=None) -> None:
+    """dst[row_map[i]] = src[i] for row_map[i] >= 0, i < row_map.numel()."""
+    dt = _elem_dtype(d)
+    n = row_map.numel()
+    _ptr(dst, "dst", dt)
+    if _rows(src, "src", d) < n:
+        raise ValueError("src has fewer rows than row_map")
+    st = load_library().moe_scatter_rows(ctypes.byref(d), n, _ptr(row_map, "row_map", torch.int32),
+                                         _ptr(src, "src", dt), dst.data_ptr(), _stream(stream))
+    _check("moe_scatter_rows", st)
+
+
+def moe_padded_layout(d: moe_dims, topk_idx, expert_offsets, pair_to_row, row_to_pair, pair_to_slot, slot_to_pair,
+                      padded_offsets, stream=None) -> None:
+    P = d.T * d.top_k
+    C = moe_capacity(d)
+    i32 = torch.int32
+    st = load_library().moe_padded_layout(
+        ctypes.byref(d), _ptr(topk_idx, "topk_idx", i32, P, nullable=P == 0),
+        _ptr(expert_offsets, "expert_offsets", i32, d.E + 1, nullable=P == 0),
+        _ptr(pair_to_row, "pair_to_row", i32, P, nullable=P == 0), _ptr(row_to_pair, "row_to_pair", i32, P, nullable=P == 0),
+        _ptr(pair_to_slot, "pair_to_slot", i32, P, nullable=P == 0), _ptr(slot_to_pair, "slot_to_pair", i32, d.E * C),
+        _ptr(padded_offsets, "padded_offsets", i32, d.E + 1), _stream(stream))
+    _check("moe_padded_layout", st)
+
+
+def moe_permute_padded(d: moe_dims, x, slot_to_pair, x_pad, stream=None) -> None:
+    dt = _elem_dtype(d)
+    C = moe_capacity(d)
+    st = load_library().moe_permute_padded(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D, nullable=d.T == 0),
+        _ptr(slot_to_pair, "slot_to_pair", torch.int32, d.E * C), _ptr(x_pad, "x_pad", dt, d.E * C * d.D),
+        _stream(stream))
+    _check("moe_permute_padded", st)
+
+
+def moe_expert_ffn_padded_up(d: moe_dims, x_pad, padded_offsets, w1, w3, h_pad, stream=None) -> None:
+    dt = _elem_dtype(d)
+    R = d.E * moe_capacity(d)
+    st = load_library().moe_expert_ffn_padded_up(
+        ctypes.byref(d), _ptr(x_pad, "x_pad", dt, R * d.D), _ptr(padded_offsets, "padded_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(h_pad, "h_pad", dt, R * d.F), _stream(stream))
+    _check("moe_expert_ffn_padded_up", st)
+
+
+def moe_expert_ffn_padded_down(d: moe_dims, h_pad, padded_offsets, w2, y_pad, stream=None) -> None:
+    dt = _elem_dtype(d)
+    R = d.E * moe_capacity(d)
+    st = load_library().moe_expert_ffn_padded_down(
+        ctypes.byref(d), _ptr(h_pad, "h_pad", dt, R * d.F), _ptr(padded_offsets, "padded_offsets", torch.int32, d.E + 1),
+        _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_pad, "y_pad", dt, R * d.D), _stream(stream))
+    _check("moe_expert_ffn_padded_down", st)

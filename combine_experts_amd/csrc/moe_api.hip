@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 101;
+constexpr int kAbiVersion = 102;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -210,6 +210,109 @@ int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* 
   if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
   if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_combine(y_perm, pair_to_row, topk_gate, y, d->T, d->D, d->top_k, d->dtype, stream));
+}
+
+int moe_dispatch_matrix(const moe_dims* d, const int32_t* topk_idx, int32_t n_src, int32_t* matrix,
+                        hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (n_src < 1 || d->T % n_src != 0) return MOE_ERR_INVALID_ARG;
+  if (!matrix || (d->T > 0 && !topk_idx)) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(matrix) || (topk_idx && !aligned4(topk_idx))) return MOE_ERR_INVALID_ARG;
+  if ((size_t)d->ep_size * sizeof(int) > 65536) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_dispatch_matrix(topk_idx, n_src, d->T / n_src, d->top_k, d->E, d->ep_size, matrix,
+                                                stream));
+}
+
+int moe_recv_layout(const moe_dims* d, int32_t n_src, int32_t rank, int64_t src_stride,
+                    const int32_t* src_expert_offsets, int32_t* recv_counts, int32_t* expert_offsets,
+                    int32_t* grouped_to_src_row, int32_t n_rows_max, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (n_src < 1 || rank < 0 || rank >= d->ep_size || src_stride < 0 || n_rows_max < 0) return MOE_ERR_INVALID_ARG;
+  if ((int64_t)n_src * src_stride > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!src_expert_offsets || !recv_counts || !expert_offsets || (n_rows_max > 0 && !grouped_to_src_row))
+    return MOE_ERR_INVALID_ARG;
+  const int epr = d->E / d->ep_size;
+  if (moe::recv_layout_lds_bytes(n_src, epr) > 65536) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_recv_layout(src_expert_offsets, n_src, d->E, d->ep_size, rank, src_stride,
+                                            recv_counts, expert_offsets, grouped_to_src_row, n_rows_max, stream));
+}
+
+static int move_rows(const moe_dims* d, bool scatter, int64_t n_rows, const int32_t* row_map, const void* src,
+                     void* dst, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (n_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (n_rows == 0) return MOE_OK;
+  if (!row_map || !src || !dst || !aligned16(src) || !aligned16(dst)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_move_rows(scatter, src, row_map, n_rows, d->D * elem_bytes(d), dst, stream));
+}
+
+int moe_gather_rows(const moe_dims* d, int64_t n_rows, const int32_t* row_map, const void* src, void* dst,
+                    hipStream_t stream) {
+  return move_rows(d, false, n_rows, row_map, src, dst, stream);
+}
+
+int moe_scatter_rows(const moe_dims* d, int64_t n_rows, const int32_t* row_map, const void* src, void* dst,
+                     hipStream_t stream) {
+  return move_rows(d, true, n_rows, row_map, src, dst, stream);
+}
+
+int moe_padded_layout(const moe_dims* d, const int32_t* topk_idx, const int32_t* expert_offsets,
+                      const int32_t* pair_to_row, const int32_t* row_to_pair, int32_t* pair_to_slot,
+                      int32_t* slot_to_pair, int32_t* padded_offsets, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;  // the padded layout needs a capacity
+  const int64_t C = capacity_of(d);
+  if ((int64_t)d->E * C > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!padded_offsets || !slot_to_pair) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!topk_idx || !expert_offsets || !pair_to_row || !row_to_pair || !pair_to_slot))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_padded_layout(topk_idx, expert_offsets, pair_to_row, row_to_pair, d->T * d->top_k,
+                                              d->E, (int)C, pair_to_slot, slot_to_pair, padded_offsets, stream));
+}
+
+int moe_permute_padded(const moe_dims* d, const void* x, const int32_t* slot_to_pair, void* x_pad,
+                       hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;
+  const int64_t n_slots = (int64_t)d->E * capacity_of(d);
+  if (n_slots > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!slot_to_pair || !x_pad || (d->T > 0 && !x)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || !aligned16(x_pad)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_permute_padded(x, slot_to_pair, n_slots, d->top_k, d->D * elem_bytes(d), x_pad,
+                                               stream));
+}
+
+static int ffn_padded(const moe_dims* d, bool up, const void* a, const int32_t* padded_offsets, const void* b0,
+                      const void* b1, void* out, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;
+  const int64_t n_slots = (int64_t)d->E * capacity_of(d);
+  if (n_slots > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!a || !padded_offsets || !b0 || !out || (up && d->act == MOE_ACT_SWIGLU && !b1)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(b0) || !aligned16(out) || (b1 && !aligned16(b1))) return MOE_ERR_INVALID_ARG;
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs f = up ? moe::FfnArgs{a, padded_offsets, b0, d->act == MOE_ACT_SWIGLU ? b1 : nullptr, out,
+                                     (int32_t)n_slots, d->E, d->D, d->F, d->act}
+                      : moe::FfnArgs{a, padded_offsets, b0, nullptr, out, (int32_t)n_slots, d->E, d->F, d->D, -1};
+  return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(f, stream) : moe::launch_ffn_f32(f, stream));
+}
+
+int moe_expert_ffn_padded_up(const moe_dims* d, const void* x_pad, const int32_t* padded_offsets, const void* w1,
+                             const void* w3, void* h_pad, hipStream_t stream) {
+  return ffn_padded(d, true, x_pad, padded_offsets, w1, w3, h_pad, stream);
+}
+
+int moe_expert_ffn_padded_down(const moe_dims* d, const void* h_pad, const int32_t* padded_offsets, const void* w2,
+                               void* y_pad, hipStream_t stream) {
+  return ffn_padded(d, false, h_pad, padded_offsets, w2, nullptr, y_pad, stream);
 }
 
 }  // extern "C"

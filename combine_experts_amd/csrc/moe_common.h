@@ -73,6 +73,18 @@ hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_per
 hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, void* y,
                           int32_t T, int32_t D, int32_t k, int dtype, hipStream_t s);
 
+hipError_t launch_dispatch_matrix(const int32_t* topk_idx, int n_src, int Ts, int k, int E, int n_dst, int32_t* matrix,
+                                  hipStream_t s);
+size_t recv_layout_lds_bytes(int n_src, int epr);
+hipError_t launch_recv_layout(const int32_t* src_off, int n_src, int E, int n_dst, int r, long long stride,
+                              int32_t* recv_counts, int32_t* exp_off, int32_t* g2s, int n_rows_max, hipStream_t s);
+hipError_t launch_move_rows(bool scatter, const void* src, const int32_t* map, long long n_rows, int row_bytes,
+                            void* dst, hipStream_t s);
+hipError_t launch_padded_layout(const int32_t* topk_idx, const int32_t* eoff, const int32_t* p2r, const int32_t* r2p,
+                                int P, int E, int C, int32_t* p2s, int32_t* s2p, int32_t* poff, hipStream_t s);
+hipError_t launch_permute_padded(const void* x, const int32_t* s2p, long long n_slots, int k, int row_bytes, void* xp,
+                                 hipStream_t s);
+
 struct FfnArgs {
   const void* a;              // x_perm (up) or h (down): [N_max, K]
   const int32_t* expert_offsets;

@@ -193,6 +193,66 @@ int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_
 int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row,
                           const float* topk_gate, void* y, hipStream_t stream);
 
+/* ---- Cluster view on one GPU: the expert-parallel data flow, emulated ----------------------------
+ * n_src source shards of T/n_src contiguous tokens each route and lay out their own tokens
+ * (moe_route / moe_dispatch_layout / moe_permute called with dims.T = T/n_src on pointer offsets);
+ * source s keeps its sent rows at rows [s*src_stride, s*src_stride + N_s) of one concatenated send
+ * buffer. Rank r (of dims.ep_size) owns experts [r*E/ep_size, (r+1)*E/ep_size) ([A2AC] dispatch
+ * example). */
+
+/* [src, dst] counts of (token, expert) pairs before any capacity cut: matrix[s*ep_size + d] = pairs
+ * of tokens [s*T/n_src, (s+1)*T/n_src) routed to experts of rank d ([A2AC] routing simulation: the
+ * per-device bincount, one row per source device). topk_idx [T, top_k]; matrix [n_src, ep_size]
+ * int32 out. Requires T % n_src == 0. Ids outside [0, E) are not counted. */
+int moe_dispatch_matrix(const moe_dims* d, const int32_t* topk_idx, int32_t n_src, int32_t* matrix,
+                        hipStream_t stream);
+
+/* Receive side of rank `rank` ([EPA2A] "The two exchanges": after the dispatch exchange a device
+ * holds one chunk per source, each sorted by its local experts, and regroups them per expert).
+ *   src_expert_offsets [n_src, E+1] int32 in: each source's own expert_offsets.
+ *   recv_counts [n_src] out: rows each source sends to this rank.
+ *   expert_offsets [E/ep_size + 1] out: offsets of this rank's local experts in the regrouped rows.
+ *   grouped_to_src_row [n_rows_max] out: send-buffer row (s*src_stride + source row) of each
+ *     regrouped row, regrouped order = (local expert, source, source row); -1 past the last row.
+ * Feed it to moe_gather_rows to run the exchange and the regroup as one pass, and to
+ * moe_scatter_rows to send expert outputs back. Unsupported: n_src*(2E/ep_size)+E/ep_size > 16384. */
+int moe_recv_layout(const moe_dims* d, int32_t n_src, int32_t rank, int64_t src_stride,
+                    const int32_t* src_expert_offsets, int32_t* recv_counts, int32_t* expert_offsets,
+                    int32_t* grouped_to_src_row, int32_t n_rows_max, hipStream_t stream);
+
+/* dst[i] = src[row_map[i]] for i < n_rows with row_map[i] >= 0 (rows of D elements of dims.dtype;
+ * a bit-exact copy; rows with -1 untouched). */
+int moe_gather_rows(const moe_dims* d, int64_t n_rows, const int32_t* row_map, const void* src, void* dst,
+                    hipStream_t stream);
+
+/* dst[row_map[i]] = src[i] for i < n_rows with row_map[i] >= 0. row_map must not repeat a target. */
+int moe_scatter_rows(const moe_dims* d, int64_t n_rows, const int32_t* row_map, const void* src, void* dst,
+                     hipStream_t stream);
+
+/* ---- Fixed-capacity (padded) layout ---------------------------------------------------------------
+ * [EPLLM] "Static Capacity Factors and Token Dropping": every expert owns C rows of an [E*C, D]
+ * buffer (C = moe_capacity, dims.capacity_factor > 0 required); unused rows are zero padding that
+ * the expert FFN still computes. Kept pairs are exactly those of the compact layout with the same C.
+ *   In: topk_idx, and moe_dispatch_layout's expert_offsets, pair_to_row, row_to_pair (same dims).
+ *   pair_to_slot [T*top_k] out: e*C + rank of the pair in its expert, or -1 when dropped.
+ *   slot_to_pair [E*C] out: the pair in each slot, -1 for padding.
+ *   padded_offsets [E+1] out: e*C (the expert_offsets of the padded buffer). */
+int moe_padded_layout(const moe_dims* d, const int32_t* topk_idx, const int32_t* expert_offsets,
+                      const int32_t* pair_to_row, const int32_t* row_to_pair, int32_t* pair_to_slot,
+                      int32_t* slot_to_pair, int32_t* padded_offsets, hipStream_t stream);
+
+/* x_pad[s] = x[slot_to_pair[s] / top_k] for filled slots, zeros for padding slots. x_pad [E*C, D]. */
+int moe_permute_padded(const moe_dims* d, const void* x, const int32_t* slot_to_pair, void* x_pad,
+                       hipStream_t stream);
+
+/* The grouped expert FFN over the padded buffer: as moe_expert_ffn_up / _down with
+ * expert_offsets = padded_offsets and E*C rows (x_pad, h_pad [E*C, F], y_pad [E*C, D]). Padding rows
+ * come out as exact zeros. Combine with moe_unpermute_combine(pair_to_row = pair_to_slot). */
+int moe_expert_ffn_padded_up(const moe_dims* d, const void* x_pad, const int32_t* padded_offsets,
+                             const void* w1, const void* w3, void* h_pad, hipStream_t stream);
+int moe_expert_ffn_padded_down(const moe_dims* d, const void* h_pad, const int32_t* padded_offsets,
+                               const void* w2, void* y_pad, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* moe_status_str(int status);
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 101
+    assert M.moe_abi_version() == 102
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -162,3 +162,25 @@ def test_route_ex_host_checks():
     d = M.make_dims(16, 64, 300, 2, 64)
     assert lib.moe_route_ex(ctypes.byref(d), fake, fake, None, fake, fake, fake, None, fake, None) == \
         M.MOE_ERR_UNSUPPORTED
+
+
+def test_cluster_and_padded_host_checks():
+    lib = M.load_library()
+    fake = ctypes.c_void_p(256)
+    d = M.make_dims(16, 64, 8, 2, 64, ep_size=4)
+    # T must split evenly over the sources
+    assert lib.moe_dispatch_matrix(ctypes.byref(d), fake, 3, fake, None) == M.MOE_ERR_INVALID_ARG
+    # rank out of range; a source stride that overflows int32 rows
+    assert lib.moe_recv_layout(ctypes.byref(d), 4, 4, 32, fake, fake, fake, fake, 8, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_recv_layout(ctypes.byref(d), 4, 0, 2**30, fake, fake, fake, fake, 8, None) == M.MOE_ERR_INVALID_ARG
+    # too many (source, local expert) pairs for the receive tables
+    big = M.make_dims(16, 64, 8192, 2, 64, ep_size=1)
+    assert lib.moe_recv_layout(ctypes.byref(big), 4, 0, 32, fake, fake, fake, fake, 8, None) == M.MOE_ERR_UNSUPPORTED
+    # the padded layout and its FFN need a capacity
+    assert lib.moe_padded_layout(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert lib.moe_permute_padded(ctypes.byref(d), fake, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_padded_up(ctypes.byref(d), fake, fake, fake, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    # row moves: misaligned buffers are rejected, zero rows are a no-op
+    assert lib.moe_gather_rows(ctypes.byref(d), 4, fake, ctypes.c_void_p(264), fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_scatter_rows(ctypes.byref(d), 0, None, None, None, None) == M.MOE_OK
