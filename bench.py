@@ -90,6 +90,99 @@ def cpu_baseline(cfg, inp, n_tokens: int):
                       f"in host memory), whole layer in float64, {dt:.1f} s"}
 
 
+def measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b):
+    """Expert parallelism emulated on one GPU at the workload's EP size: every source shard lays out
+    its own tokens into one concatenated send buffer; the exchange of all ranks (with each rank's
+    per-expert regroup) is one row gather over all N rows, the return one row scatter."""
+    n_src = cfg.ep_size
+    ts = cfg.T // n_src
+    k, E, D = cfg.top_k, cfg.E, cfg.D
+    stride = ts * k
+    dev = "cuda"
+    i32 = dict(dtype=torch.int32, device=dev)
+    d_src = M.dims_from_config(cfg.replace(T=ts))
+    src_off = torch.empty((n_src, E + 1), **i32)
+    p2r = torch.empty((n_src, ts * k), **i32)
+    r2p = torch.empty((n_src, ts * k), **i32)
+    cnt, rc, ro = torch.empty(E, **i32), torch.empty(cfg.ep_size, **i32), torch.empty(cfg.ep_size + 1, **i32)
+    ws = torch.empty(max(1, M.moe_workspace_size(d_src, M.MOE_STAGE_LAYOUT)), dtype=torch.uint8, device=dev)
+    send = torch.empty((n_src * stride, D), dtype=W.torch_dtype(cfg.dtype), device=dev)
+    for s in range(n_src):
+        M.moe_dispatch_layout(d_src, buf.topk_idx[s * ts * k:(s + 1) * ts * k], cnt, src_off[s], rc, ro, p2r[s], r2p[s],
+                              ws, stream)
+        M.moe_permute(d_src, inp["x"][s * ts:(s + 1) * ts], p2r[s], send[s * stride:(s + 1) * stride], stream)
+    matrix = torch.empty((n_src, cfg.ep_size), **i32)
+    t_matrix = time_calls(lambda: M.moe_dispatch_matrix(d, buf.topk_idx, n_src, matrix, stream))
+    epr = E // cfg.ep_size
+    g2s = torch.empty(cfg.T * k, **i32)
+    recv_counts, eoff = torch.empty(n_src, **i32), torch.empty(epr + 1, **i32)
+    t_recv = time_calls(lambda: M.moe_recv_layout(d, n_src, 0, stride, src_off, recv_counts, eoff, g2s, stream))
+    # all ranks' regrouped rows, rank after rank: one map over every sent row
+    maps = []
+    for r in range(cfg.ep_size):
+        M.moe_recv_layout(d, n_src, r, stride, src_off, recv_counts, eoff, g2s, stream)
+        torch.cuda.synchronize()
+        maps.append(g2s[:int(eoff[-1])].clone())
+    full_map = torch.cat(maps)
+    n = full_map.numel()
+    grouped = torch.empty((n, D), dtype=send.dtype, device=dev)
+    back = torch.empty_like(send)
+    t_gather = time_calls(lambda: M.moe_gather_rows(d, full_map, send, grouped, stream))
+    t_scatter = time_calls(lambda: M.moe_scatter_rows(d, full_map, grouped, back, stream))
+    moved = 2.0 * n * D * b + n * 4
+    out = {"n_src": n_src, "rows": n, "dispatch_matrix_ms": t_matrix, "recv_layout_ms": t_recv,
+           "exchange_gather_ms": t_gather, "return_scatter_ms": t_scatter,
+           "exchange_gbps": round(moved / (t_gather * 1e-3) / 1e9, 1),
+           "return_gbps": round(moved / (t_scatter * 1e-3) / 1e9, 1)}
+    del send, grouped, back
+    return out
+
+
+def measure_padded(M, W, torch, cfg, inp, stream, time_calls, cf=1.25):
+    """The fixed-capacity padded layout against the compact layout with the same capacity."""
+    c = cfg.replace(capacity_factor=cfg.capacity_factor if cfg.capacity_factor > 0 else cf)
+    d = M.dims_from_config(c)
+    buf = M.MoELayerBuffers(d, device="cuda")
+    C = M.moe_capacity(d)
+    R = c.E * C
+    dt = W.torch_dtype(c.dtype)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    p2s, s2p, poff = torch.empty(c.T * c.top_k, **i32), torch.empty(R, **i32), torch.empty(c.E + 1, **i32)
+    x_pad = torch.empty((R, c.D), dtype=dt, device="cuda")
+    h_pad = torch.empty((R, c.F), dtype=dt, device="cuda")
+    y_pad = torch.empty((R, c.D), dtype=dt, device="cuda")
+    M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, None, stream)
+
+    def layout():
+        M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
+                              buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
+
+    def compact():
+        layout()
+        M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+        M.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], buf.h, stream)
+        M.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm, stream)
+        M.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
+
+    def padded():
+        layout()
+        M.moe_padded_layout(d, buf.topk_idx, buf.expert_offsets, buf.pair_to_row, buf.row_to_pair, p2s, s2p, poff,
+                            stream)
+        M.moe_permute_padded(d, inp["x"], s2p, x_pad, stream)
+        M.moe_expert_ffn_padded_up(d, x_pad, poff, inp["w1"], inp["w3"], h_pad, stream)
+        M.moe_expert_ffn_padded_down(d, h_pad, poff, inp["w2"], y_pad, stream)
+        M.moe_unpermute_combine(d, y_pad, p2s, buf.topk_gate, buf.y, stream, n_rows=R)
+
+    t_compact = time_calls(compact, reps=5)
+    t_padded = time_calls(padded, reps=5)
+    N = int(buf.expert_offsets[-1].item())
+    out = {"capacity_factor": c.capacity_factor, "C": C, "slots": R, "kept": N,
+           "padding_frac": round((R - N) / R, 4), "dropped": c.T * c.top_k - N,
+           "compact_ms": round(t_compact, 4), "padded_ms": round(t_padded, 4)}
+    del buf, x_pad, h_pad, y_pad
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,8 +308,21 @@ def main(argv=None):
         "load_balance": time_calls(lambda: M.moe_load_balance(d, buf.expert_counts, part, 0.01, stats, 0.0, None,
                                                               stream)),
     }
+    # the routing the step left in buf is restored before the cluster and padded measurements
+    M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, None, stream)
+    M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
+                          buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
+    cluster = measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b)
+    padded = measure_padded(M, W, torch, cfg, inp, stream, time_calls)
+    extra_ms.update({"dispatch_matrix": cluster["dispatch_matrix_ms"], "recv_layout": cluster["recv_layout_ms"],
+                     "exchange_gather": cluster["exchange_gather_ms"], "return_scatter": cluster["return_scatter_ms"]})
     for s_, v in extra_ms.items():
-        log(f"[bench]   {s_:12s} {v * 1e3:9.1f} us (outside the step)")
+        log(f"[bench]   {s_:15s} {v * 1e3:9.1f} us (outside the step)")
+    log(f"[bench] emulated exchange over {cluster['n_src']} sources: {cluster['rows']} rows, gather "
+        f"{cluster['exchange_gbps']:.0f} GB/s, scatter {cluster['return_gbps']:.0f} GB/s")
+    log(f"[bench] padded layout at CF {padded['capacity_factor']}: C={padded['C']}, padding "
+        f"{padded['padding_frac']:.1%}, dropped {padded['dropped']}; compact path {padded['compact_ms']:.3f} ms, "
+        f"padded path {padded['padded_ms']:.3f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -236,6 +342,8 @@ def main(argv=None):
                    "kept_rows": N, "parallelism": "1 GPU"},
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
         "extra_stage_ms": {s: round(v, 4) for s, v in extra_ms.items()},
+        "cluster_emulation": cluster,
+        "padded_capacity": padded,
         "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
         "gemm_mfma_frac": round(ffn_tflops / peak, 4),
         "roofline": roofline,
