@@ -24,6 +24,7 @@ __all__ = [
     "combine", "comm_volume_elements", "dispatch_volume_bytes", "layer_forward",
     "router_probabilities", "load_balance_stats", "update_select_bias", "selection_key",
     "source_shards", "recv_layout", "cluster_forward", "padded_layout", "permute_padded",
+    "shared_expert_ffn", "layer_forward_chunked",
 ]
 
 GATE_SOFTMAX_TOPK = 0
@@ -626,8 +627,43 @@ def dispatch_volume_bytes(n_remote: int, D: int, elem_bytes: int) -> int:
 # The whole layer
 # ----------------------------------------------------------------------------------------------
 
+def shared_expert_ffn(x, w1, w3, w2, act: int) -> np.ndarray:
+    """A shared expert: the same expert FFN applied to every token, with gate 1.
+
+    READING: [EPLLM] "Overlapping All-to-All with Computation" names the shared
+    expert computation that the dispatch of the next layer overlaps, without its
+    formula; it is read as DeepSeek-V3's shared expert: one always-active
+    expert of the routed experts' kind whose output is added to the routed sum.
+    """
+    return _expert_rows(as_f64(x), w1, w3, w2, act)
+
+
+def layer_forward_chunked(inputs: Dict, cfg, n_chunks: int) -> Dict[str, np.ndarray]:
+    """The layer on n_chunks contiguous micro-batches of T/n_chunks tokens, one after the other.
+
+    [EPA2A] (DeepSeek-V3 splits the work into micro-batches so that the
+    exchange of one hides behind the computation of another). Each micro-batch
+    is routed, laid out and combined on its own; with no capacity limit the
+    result equals the whole-batch layer.
+    """
+    T = cfg.T
+    if n_chunks < 1 or T % n_chunks != 0:
+        raise ValueError("T must split evenly into the micro-batches")
+    tc = T // n_chunks
+    ys = []
+    for c in range(n_chunks):
+        sub = {k: v for k, v in inputs.items()}
+        sub["x"] = inputs["x"][c * tc:(c + 1) * tc]
+        ys.append(layer_forward(sub, cfg.replace(T=tc))["y"])
+    return {"y": np.concatenate(ys, axis=0)}
+
+
 def layer_forward(inputs: Dict, cfg) -> Dict[str, np.ndarray]:
-    """Router -> layout -> permute -> expert FFN -> combine on one device, all in float64."""
+    """Router -> layout -> permute -> expert FFN -> combine on one device, all in float64.
+
+    With shared-expert weights in ``inputs`` (shared_w1, shared_w3, shared_w2)
+    the shared expert's output is added to the routed sum.
+    """
     r = route(inputs["x"], inputs["w_gate"], inputs.get("bias"), cfg.top_k, cfg.gate,
               cfg.n_groups, cfg.topk_groups)
     C = capacity(cfg.capacity_factor, cfg.T, cfg.top_k, cfg.E)
@@ -635,6 +671,9 @@ def layer_forward(inputs: Dict, cfg) -> Dict[str, np.ndarray]:
     xp = permute(as_f64(inputs["x"]), lay["row_to_pair"], cfg.top_k, lay["n_kept"])
     yp = expert_ffn(xp, lay["expert_offsets"], inputs["w1"], inputs.get("w3"), inputs["w2"], cfg.act)
     y = combine(yp, lay["pair_to_row"], r["topk_gate"], cfg.T, cfg.top_k)
+    if inputs.get("shared_w1") is not None:
+        y = y + shared_expert_ffn(inputs["x"], inputs["shared_w1"], inputs.get("shared_w3"), inputs["shared_w2"],
+                                  cfg.act)
     out = dict(r)
     out.update(lay)
     out.update({"x_perm": xp, "y_perm": yp, "y": y})

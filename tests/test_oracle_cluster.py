@@ -126,3 +126,37 @@ def test_padded_forward_equals_compact_forward_with_capacity(cf):
     assert np.all(yp[pad["slot_to_pair"] < 0] == 0)
     y = O.combine(yp, pad["pair_to_slot"], one["topk_gate"], cfg.T, cfg.top_k)
     np.testing.assert_allclose(y, one["y"], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------------
+# Shared expert and micro-batches
+# ------------------------------------------------------------------------------------------------
+
+def test_shared_expert_is_a_dense_one_expert_layer():
+    # one expert, top-1, gate 1 (k = 1 softmax) routes every token to it: the dense layer
+    cfg = _tiny(E=1, top_k=1, ep_size=1)
+    inp = W.make_inputs(cfg, "cpu")
+    dense = O.layer_forward(inp, cfg)["y"]
+    shared = O.shared_expert_ffn(inp["x"], inp["w1"][0], inp["w3"][0], inp["w2"][0], cfg.act)
+    np.testing.assert_allclose(shared, dense, rtol=1e-12, atol=1e-14)
+
+
+def test_shared_expert_adds_to_the_routed_sum():
+    cfg = _tiny(shared_F=40)
+    inp = W.make_inputs(cfg, "cpu")
+    routed = O.layer_forward({k: v for k, v in inp.items() if not k.startswith("shared")}, cfg)["y"]
+    both = O.layer_forward(inp, cfg)["y"]
+    sh = O.shared_expert_ffn(inp["x"], inp["shared_w1"], inp["shared_w3"], inp["shared_w2"], cfg.act)
+    np.testing.assert_allclose(both, routed + sh, rtol=1e-13, atol=1e-15)
+    # a zero shared down-projection contributes nothing
+    z = dict(inp)
+    z["shared_w2"] = inp["shared_w2"] * 0
+    np.testing.assert_array_equal(O.layer_forward(z, cfg)["y"], routed)
+
+
+@pytest.mark.parametrize("n_chunks", [1, 2, 4, 8])
+def test_micro_batches_equal_the_whole_batch(n_chunks):
+    cfg = _tiny(shared_F=24, gate=W.GATE_SIGMOID_TOPK, n_groups=4, topk_groups=2)
+    inp = W.make_inputs(cfg, "cpu")
+    np.testing.assert_allclose(O.layer_forward_chunked(inp, cfg, n_chunks)["y"], O.layer_forward(inp, cfg)["y"],
+                               rtol=1e-12, atol=1e-14)

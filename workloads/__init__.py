@@ -71,6 +71,7 @@ class MoEConfig:
     bias: str = "none"                # "none" | "normal0.5" | "zipf"
     seed: int = 0
     desc: str = ""
+    shared_F: int = 0                 # > 0 : one shared expert of this hidden size on every token
 
     def replace(self, **kw) -> "MoEConfig":
         return dataclasses.replace(self, **kw)
@@ -187,7 +188,8 @@ def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict
 
     x [T,D], w_gate [E,D] in the config dtype; bias [E] float32 or None;
     w1, w3 [E,F,D] and w2 [E,D,F] (w3 None for GELU experts). Expert weights
-    are drawn one expert at a time into preallocated stacks.
+    are drawn one expert at a time into preallocated stacks. With shared_F > 0
+    also shared_w1, shared_w3 [shared_F, D] and shared_w2 [D, shared_F].
     """
     dt = torch_dtype(cfg.dtype)
     out: Dict[str, Optional[torch.Tensor]] = {}
@@ -206,6 +208,12 @@ def make_inputs(cfg: MoEConfig, device="cpu", with_experts: bool = True) -> Dict
             w2[e].copy_(c)
             del a, b, c
         out["w1"], out["w3"], out["w2"] = w1, w3, w2
+    if cfg.shared_F > 0:
+        fs = cfg.shared_F
+        out["shared_w1"] = _normal((fs, cfg.D), 0.02, dt, device, cfg.seed, "shared_w1")
+        out["shared_w3"] = (_normal((fs, cfg.D), 0.02, dt, device, cfg.seed, "shared_w3")
+                            if cfg.act == ACT_SWIGLU else None)
+        out["shared_w2"] = _normal((cfg.D, fs), 0.02, dt, device, cfg.seed, "shared_w2")
     return out
 
 
