@@ -9,9 +9,10 @@ from ._lib import (  # noqa: F401
     moe_abi_version, moe_status_str, moe_capacity, moe_workspace_size, moe_route, moe_route_ex,
     moe_load_balance, moe_dispatch_layout, moe_dispatch_matrix, moe_recv_layout, moe_gather_rows, moe_scatter_rows,
     moe_padded_layout, moe_permute_padded, moe_expert_ffn_padded_up, moe_expert_ffn_padded_down,
+    moe_unpermute_combine_add, moe_layer_forward, moe_layer_args, moe_event_create, moe_event_destroy,
     moe_permute, moe_expert_ffn, moe_expert_ffn_up, moe_expert_ffn_down, moe_unpermute_combine,
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL, MOE_ACT_SWIGLU, MOE_ACT_GELU,
     MOE_F32, MOE_BF16, MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS,
 )
-from .layer import MoELayerBuffers, forward  # noqa: F401
+from .layer import MoELayerBuffers, forward, LayerExecutor  # noqa: F401

@@ -37,6 +37,15 @@ class moe_dims(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+class moe_layer_args(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "w_gate", "bias", "w1", "w3", "w2", "y", "topk_idx", "topk_gate",
+                                  "pair_to_row", "row_to_pair", "x_perm", "h", "y_perm", "expert_counts",
+                                  "expert_offsets", "rank_counts", "rank_offsets", "layout_ws")] + \
+        [("layout_ws_bytes", ctypes.c_size_t)] + \
+        [(n, _P) for n in ("shared_w1", "shared_w3", "shared_w2")] + [("shared_F", ctypes.c_int32)] + \
+        [(n, _P) for n in ("shared_h", "shared_y", "shared_offsets")]
 _SIG = {
     "moe_abi_version": (ctypes.c_int, []),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -54,6 +63,11 @@ _SIG = {
     "moe_permute_padded": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
     "moe_expert_ffn_padded_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_padded_down": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+    "moe_unpermute_combine_add": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_layer_args), ctypes.c_int32, _P,
+                                         _P, _P]),
+    "moe_event_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "moe_event_destroy": (ctypes.c_int, [_P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
@@ -342,3 +356,37 @@ def moe_expert_ffn_padded_down(d: moe_dims, h_pad, padded_offsets, w2, y_pad, st
         ctypes.byref(d), _ptr(h_pad, "h_pad", dt, R * d.F), _ptr(padded_offsets, "padded_offsets", torch.int32, d.E + 1),
         _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_pad, "y_pad", dt, R * d.D), _stream(stream))
     _check("moe_expert_ffn_padded_down", st)
+
+
+
+def moe_unpermute_combine_add(d: moe_dims, y_perm, pair_to_row, topk_gate, addend, y, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_unpermute_combine_add(
+        ctypes.byref(d), _ptr(y_perm, "y_perm", dt, P * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        _ptr(topk_gate, "topk_gate", torch.float32, P), _ptr(addend, "addend", dt, d.T * d.D, nullable=True),
+        _ptr(y, "y", dt, d.T * d.D), _stream(stream))
+    _check("moe_unpermute_combine_add", st)
+
+
+def moe_event_create() -> int:
+    e = _P()
+    _check("moe_event_create", load_library().moe_event_create(ctypes.byref(e)))
+    return e.value
+
+
+def moe_event_destroy(event: int) -> None:
+    _check("moe_event_destroy", load_library().moe_event_destroy(event))
+
+
+def moe_layer_forward(d: moe_dims, args: moe_layer_args, n_chunks: int, stream=None, side_stream=None,
+                      events=None) -> None:
+    """Marshalling only: ``args`` is filled by ``layer.LayerExecutor`` from its torch buffers."""
+    ev = None
+    if side_stream is not None:
+        if events is None or len(events) < 2 * n_chunks:
+            raise ValueError("two events per micro-batch are needed with a side stream")
+        ev = (_P * len(events))(*events)
+    st = load_library().moe_layer_forward(ctypes.byref(d), ctypes.byref(args), int(n_chunks), _stream(stream),
+                                          None if side_stream is None else _stream(side_stream), ev)
+    _check("moe_layer_forward", st)

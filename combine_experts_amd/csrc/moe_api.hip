@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 102;
+constexpr int kAbiVersion = 103;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -201,15 +201,21 @@ int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_
   return moe_expert_ffn_down(d, ws, expert_offsets, w2, y_perm, stream);
 }
 
-int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row, const float* topk_gate,
-                          void* y, hipStream_t stream) {
+int moe_unpermute_combine_add(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row,
+                              const float* topk_gate, const void* addend, void* y, hipStream_t stream) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (d->T == 0) return MOE_OK;
   if (!y_perm || !pair_to_row || !topk_gate || !y) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(y_perm) || !aligned16(y) || (addend && !aligned16(addend))) return MOE_ERR_INVALID_ARG;
   if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_combine(y_perm, pair_to_row, topk_gate, y, d->T, d->D, d->top_k, d->dtype, stream));
+  return hip_status(
+      moe::launch_combine(y_perm, pair_to_row, topk_gate, addend, y, d->T, d->D, d->top_k, d->dtype, stream));
+}
+
+int moe_unpermute_combine(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row, const float* topk_gate,
+                          void* y, hipStream_t stream) {
+  return moe_unpermute_combine_add(d, y_perm, pair_to_row, topk_gate, nullptr, y, stream);
 }
 
 int moe_dispatch_matrix(const moe_dims* d, const int32_t* topk_idx, int32_t n_src, int32_t* matrix,

@@ -70,7 +70,7 @@ hipError_t launch_load_balance(const int32_t* expert_counts, const float* prob_p
 
 hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_perm, int32_t T, int32_t D,
                           int32_t k, int dtype, hipStream_t s);
-hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, void* y,
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, const void* add, void* y,
                           int32_t T, int32_t D, int32_t k, int dtype, hipStream_t s);
 
 hipError_t launch_dispatch_matrix(const int32_t* topk_idx, int n_src, int Ts, int k, int E, int n_dst, int32_t* matrix,

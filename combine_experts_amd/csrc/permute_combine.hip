@@ -53,10 +53,12 @@ __global__ void __launch_bounds__(256) permute_kernel(const u32x4* __restrict__ 
   }
 }
 
-template <typename T>
+// ADD: y[t] also takes add[t] (a shared expert's output), summed in float32 after the k slots and
+// before the one rounding.
+template <typename T, bool ADD>
 __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ yp, const int32_t* __restrict__ p2r,
-                                                      const float* __restrict__ gate, T* __restrict__ y, int T_,
-                                                      int D, int k) {
+                                                      const float* __restrict__ gate, const T* __restrict__ add,
+                                                      T* __restrict__ y, int T_, int D, int k) {
   constexpr int VN = Vec<T>::N;
   const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
   const int row_chunks = D / VN;
@@ -80,6 +82,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ yp, 
             const T* e = reinterpret_cast<const T*>(&raw);
 #pragma unroll
             for (int i = 0; i < VN; ++i) acc[u][i] = fmaf(g, to_f32<T>(e[i]), acc[u][i]);
+          }
+        }
+      }
+      if constexpr (ADD) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          if (c < row_chunks) {
+            const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(add + (size_t)t * D) + c);
+            const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[u][i] += to_f32<T>(e[i]);
           }
         }
       }
@@ -115,16 +129,22 @@ hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_per
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, void* y, int32_t T,
-                          int32_t D, int32_t k, int dtype, hipStream_t s) {
+template <typename T>
+void launch_combine_t(const void* y_perm, const int32_t* pair_to_row, const float* gate, const void* add, void* y,
+                      int32_t T_, int32_t D, int32_t k, hipStream_t s) {
+  if (add != nullptr)
+    hipLaunchKernelGGL((combine_kernel<T, true>), dim3(grid_for(T_)), dim3(256), 0, s, (const T*)y_perm, pair_to_row,
+                       gate, (const T*)add, (T*)y, T_, D, k);
+  else
+    hipLaunchKernelGGL((combine_kernel<T, false>), dim3(grid_for(T_)), dim3(256), 0, s, (const T*)y_perm, pair_to_row,
+                       gate, nullptr, (T*)y, T_, D, k);
+}
+
+hipError_t launch_combine(const void* y_perm, const int32_t* pair_to_row, const float* gate, const void* add, void* y,
+                          int32_t T, int32_t D, int32_t k, int dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (dtype == MOE_BF16) {
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid_for(T)), dim3(256), 0, s, (const bf16_t*)y_perm,
-                       pair_to_row, gate, (bf16_t*)y, T, D, k);
-  } else {
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid_for(T)), dim3(256), 0, s, (const float*)y_perm,
-                       pair_to_row, gate, (float*)y, T, D, k);
-  }
+  if (dtype == MOE_BF16) launch_combine_t<bf16_t>(y_perm, pair_to_row, gate, add, y, T, D, k, s);
+  else launch_combine_t<float>(y_perm, pair_to_row, gate, add, y, T, D, k, s);
   return hipGetLastError();
 }
 

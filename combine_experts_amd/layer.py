@@ -50,3 +50,66 @@ def forward(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, stream=None) -> t
     L.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, w2, buf.y_perm, stream)
     L.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
     return buf.y
+
+
+class LayerExecutor:
+    """Buffers, streams and events for ``moe_layer_forward`` (micro-batches, optional side stream and
+    shared expert). Allocates once with torch; every call only enqueues the library's kernels."""
+
+    def __init__(self, d: L.moe_dims, n_chunks: int = 1, two_streams: bool = False, shared_F: int = 0,
+                 device="cuda"):
+        if d.T % n_chunks != 0:
+            raise ValueError("T must split evenly into the micro-batches")
+        self.d, self.n_chunks = d, n_chunks
+        dt = torch.bfloat16 if d.dtype == L.MOE_BF16 else torch.float32
+        P, E, ep = d.T * d.top_k, d.E, d.ep_size
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty(P, **i32)
+        self.topk_gate = torch.empty(P, dtype=torch.float32, device=device)
+        self.pair_to_row = torch.empty(P, **i32)
+        self.row_to_pair = torch.empty(P, **i32)
+        self.x_perm = torch.empty((P, d.D), dtype=dt, device=device)
+        self.h = torch.empty((P, d.F), dtype=dt, device=device)
+        self.y_perm = torch.empty((P, d.D), dtype=dt, device=device)
+        self.y = torch.empty((d.T, d.D), dtype=dt, device=device)
+        self.expert_counts = torch.empty((n_chunks, E), **i32)
+        self.expert_offsets = torch.empty((n_chunks, E + 1), **i32)
+        self.rank_counts = torch.empty((n_chunks, ep), **i32)
+        self.rank_offsets = torch.empty((n_chunks, ep + 1), **i32)
+        dc = L.moe_dims.from_buffer_copy(d)
+        dc.T = d.T // n_chunks
+        ws = (L.moe_workspace_size(dc, L.MOE_STAGE_LAYOUT) + 255) // 256 * 256
+        self.layout_ws = torch.empty(max(1, ws * n_chunks), dtype=torch.uint8, device=device)
+        self.shared_F = shared_F
+        if shared_F > 0:
+            self.shared_h = torch.empty((d.T, shared_F), dtype=dt, device=device)
+            self.shared_y = torch.empty((d.T, d.D), dtype=dt, device=device)
+            self.shared_offsets = torch.tensor([0, d.T // n_chunks], **i32)
+        self.side = torch.cuda.Stream(device=device) if two_streams else None
+        self.events = [L.moe_event_create() for _ in range(2 * n_chunks)] if two_streams else None
+
+    def __del__(self):
+        for e in (self.events or []):
+            try:
+                L.moe_event_destroy(e)
+            except Exception:
+                pass
+        self.events = None
+
+    def forward(self, x, w_gate, bias, w1, w3, w2, shared=None, stream=None) -> torch.Tensor:
+        """shared: (shared_w1, shared_w3, shared_w2) or None."""
+        p = lambda t: None if t is None else t.data_ptr()
+        a = L.moe_layer_args()
+        a.x, a.w_gate, a.bias, a.w1, a.w3, a.w2, a.y = p(x), p(w_gate), p(bias), p(w1), p(w3), p(w2), p(self.y)
+        for n in ("topk_idx", "topk_gate", "pair_to_row", "row_to_pair", "x_perm", "h", "y_perm", "expert_counts",
+                  "expert_offsets", "rank_counts", "rank_offsets", "layout_ws"):
+            setattr(a, n, p(getattr(self, n)))
+        a.layout_ws_bytes = self.layout_ws.numel()
+        if shared is not None:
+            if self.shared_F <= 0:
+                raise ValueError("executor built without a shared expert")
+            a.shared_w1, a.shared_w3, a.shared_w2 = p(shared[0]), p(shared[1]), p(shared[2])
+            a.shared_F = self.shared_F
+            a.shared_h, a.shared_y, a.shared_offsets = p(self.shared_h), p(self.shared_y), p(self.shared_offsets)
+        L.moe_layer_forward(self.d, a, self.n_chunks, stream, self.side, self.events)
+        return self.y

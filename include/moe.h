@@ -253,6 +253,69 @@ int moe_expert_ffn_padded_up(const moe_dims* d, const void* x_pad, const int32_t
 int moe_expert_ffn_padded_down(const moe_dims* d, const void* h_pad, const int32_t* padded_offsets,
                                const void* w2, void* y_pad, hipStream_t stream);
 
+/* moe_unpermute_combine plus an addend: y[t] = sum_j g[t,j] * y_perm[row] + addend[t], summed in
+ * float32 (the k slots in slot order, then the addend) and rounded once. addend [T, D] dtype, or NULL
+ * (then this is moe_unpermute_combine). Used for a shared expert's output. */
+int moe_unpermute_combine_add(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row,
+                              const float* topk_gate, const void* addend, void* y, hipStream_t stream);
+
+/* ---- Layer executor: micro-batches on two streams, optional shared expert --------------------------
+ * [EPA2A] (DeepSeek-V3 splits the work into micro-batches so one micro-batch's exchange hides behind
+ * another's computation); [EPLLM] "Overlapping All-to-All with Computation" (dual-stream
+ * scheduling; the shared expert's computation runs while the dispatch is in flight). On one GPU the
+ * permute and the combine stand in for the two exchanges. With n_chunks micro-batches of
+ * T/n_chunks tokens, micro-batch c's grouped FFN runs on `side_stream` while `stream` routes, lays
+ * out and permutes micro-batch c+1, runs the shared expert and combines micro-batch c-1.
+ *
+ * Buffers (all caller-owned, device): the whole-batch buffers of the five steps; micro-batch c uses
+ * entries / rows [c*Tc*top_k, (c+1)*Tc*top_k) of topk_idx, topk_gate, pair_to_row, row_to_pair,
+ * x_perm, h, y_perm (whose row indices are local to the micro-batch), and slice c of the per-batch
+ * arrays expert_counts [n_chunks, E], expert_offsets [n_chunks, E+1], rank_counts [n_chunks, ep],
+ * rank_offsets [n_chunks, ep+1], layout_ws [n_chunks, roundup256(moe_workspace_size(LAYOUT) at
+ * T = Tc)]. A capacity factor applies per micro-batch (C from Tc). */
+typedef struct moe_layer_args {
+  const void* x;             /* [T, D] */
+  const void* w_gate;        /* [E, D] */
+  const float* bias;         /* [E] or NULL */
+  const void* w1;            /* [E, F, D] */
+  const void* w3;            /* [E, F, D] or NULL (GELU) */
+  const void* w2;            /* [E, D, F] */
+  void* y;                   /* [T, D] out */
+  int32_t* topk_idx;         /* [T*top_k] */
+  float* topk_gate;          /* [T*top_k] */
+  int32_t* pair_to_row;      /* [T*top_k] */
+  int32_t* row_to_pair;      /* [T*top_k] */
+  void* x_perm;              /* [T*top_k, D] */
+  void* h;                   /* [T*top_k, F] */
+  void* y_perm;              /* [T*top_k, D] */
+  int32_t* expert_counts;    /* [n_chunks, E] */
+  int32_t* expert_offsets;   /* [n_chunks, E+1] */
+  int32_t* rank_counts;      /* [n_chunks, ep_size] */
+  int32_t* rank_offsets;     /* [n_chunks, ep_size+1] */
+  void* layout_ws;
+  size_t layout_ws_bytes;
+  /* optional shared expert (shared_w1 == NULL: none), hidden size shared_F, same activation */
+  const void* shared_w1;     /* [shared_F, D] */
+  const void* shared_w3;     /* [shared_F, D] or NULL (GELU) */
+  const void* shared_w2;     /* [D, shared_F] */
+  int32_t shared_F;
+  void* shared_h;            /* [T, shared_F] scratch */
+  void* shared_y;            /* [T, D] scratch */
+  const int32_t* shared_offsets; /* int32 [2] = {0, T/n_chunks} */
+} moe_layer_args;
+
+/* Runs the layer as above. side_stream NULL: everything on `stream`, micro-batch after micro-batch.
+ * Otherwise `events` holds 2*n_chunks events from moe_event_create (or hipEventCreateWithFlags with
+ * hipEventDisableTiming), not shared with a concurrent call. All work of the call is ordered before
+ * later work on `stream`. Requires T % n_chunks == 0; the rest as the five entry points. */
+int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chunks, hipStream_t stream,
+                      hipStream_t side_stream, const hipEvent_t* events);
+
+/* Host helpers for the executor's events (hipEventCreateWithFlags(.., hipEventDisableTiming) and
+ * hipEventDestroy). */
+int moe_event_create(hipEvent_t* event);
+int moe_event_destroy(hipEvent_t event);
+
 /* Static description of a status code. */
 const char* moe_status_str(int status);
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 102
+    assert M.moe_abi_version() == 103
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -184,3 +184,25 @@ def test_cluster_and_padded_host_checks():
     # row moves: misaligned buffers are rejected, zero rows are a no-op
     assert lib.moe_gather_rows(ctypes.byref(d), 4, fake, ctypes.c_void_p(264), fake, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_scatter_rows(ctypes.byref(d), 0, None, None, None, None) == M.MOE_OK
+
+
+def test_layer_args_struct_layout():
+    # 19 pointers, a size_t, 3 pointers, an int32 (padded to 8), 3 pointers
+    assert ctypes.sizeof(M.moe_layer_args) == 19 * 8 + 8 + 3 * 8 + 8 + 3 * 8
+    assert M.moe_layer_args.layout_ws_bytes.offset == 19 * 8
+    assert M.moe_layer_args.shared_F.offset == 19 * 8 + 8 + 3 * 8
+
+
+def test_layer_forward_host_checks():
+    lib = M.load_library()
+    d = M.make_dims(16, 64, 8, 2, 64)
+    a = M.moe_layer_args()
+    # T must split evenly; a side stream needs events; a layout workspace is required
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(a), 3, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(a), 2, None, ctypes.c_void_p(8), None) == \
+        M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(a), 2, None, None, None) == M.MOE_ERR_WORKSPACE
+    # a shared expert without its scratch buffers
+    a.layout_ws, a.layout_ws_bytes = 256, 1 << 20
+    a.shared_w1, a.shared_F = 256, 64
+    assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(a), 2, None, None, None) == M.MOE_ERR_INVALID_ARG
