@@ -183,6 +183,27 @@ def measure_padded(M, W, torch, cfg, inp, stream, time_calls, cf=1.25):
     return out
 
 
+def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
+    """The layer executor: one stream vs n_chunks micro-batches on two streams, without and with a
+    shared expert of the routed experts' hidden size."""
+    d = M.dims_from_config(cfg)
+    fs = cfg.F
+    sh_cfg = cfg.replace(shared_F=fs)
+    sh = W.make_inputs(sh_cfg, "cuda", with_experts=False)
+    shared = (sh["shared_w1"], sh["shared_w3"], sh["shared_w2"])
+    out = {"n_chunks": n_chunks, "shared_F": fs}
+    for key, nc, two, use_sh in (("sequential_ms", 1, False, False), ("overlapped_ms", n_chunks, True, False),
+                                 ("shared_sequential_ms", 1, False, True), ("shared_overlapped_ms", n_chunks, True, True),
+                                 ("shared_concurrent_ms", 1, True, True)):
+        ex = M.LayerExecutor(d, n_chunks=nc, two_streams=two, shared_F=fs if use_sh else 0)
+        out[key] = round(time_calls(lambda: ex.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
+                                                       inp["w2"], shared=shared if use_sh else None, stream=stream),
+                                    reps=5), 4)
+        del ex
+    del sh
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -314,6 +335,7 @@ def main(argv=None):
                           buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
     cluster = measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b)
     padded = measure_padded(M, W, torch, cfg, inp, stream, time_calls)
+    overlap = measure_overlap(M, W, torch, cfg, inp, stream, time_calls)
     extra_ms.update({"dispatch_matrix": cluster["dispatch_matrix_ms"], "recv_layout": cluster["recv_layout_ms"],
                      "exchange_gather": cluster["exchange_gather_ms"], "return_scatter": cluster["return_scatter_ms"]})
     for s_, v in extra_ms.items():
@@ -323,6 +345,10 @@ def main(argv=None):
     log(f"[bench] padded layout at CF {padded['capacity_factor']}: C={padded['C']}, padding "
         f"{padded['padding_frac']:.1%}, dropped {padded['dropped']}; compact path {padded['compact_ms']:.3f} ms, "
         f"padded path {padded['padded_ms']:.3f} ms")
+    log(f"[bench] executor: 1 stream {overlap['sequential_ms']:.3f} ms, {overlap['n_chunks']} micro-batches on 2 streams "
+        f"{overlap['overlapped_ms']:.3f} ms; with a shared expert (F={overlap['shared_F']}) "
+        f"{overlap['shared_sequential_ms']:.3f} / {overlap['shared_overlapped_ms']:.3f} ms, shared expert beside the "
+        f"routed FFN on one batch {overlap['shared_concurrent_ms']:.3f} ms")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,6 +370,7 @@ def main(argv=None):
         "extra_stage_ms": {s: round(v, 4) for s, v in extra_ms.items()},
         "cluster_emulation": cluster,
         "padded_capacity": padded,
+        "overlap": overlap,
         "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
         "gemm_mfma_frac": round(ffn_tflops / peak, 4),
         "roofline": roofline,
