@@ -25,6 +25,7 @@ __all__ = [
     "router_probabilities", "load_balance_stats", "update_select_bias", "selection_key",
     "source_shards", "recv_layout", "cluster_forward", "padded_layout", "permute_padded",
     "shared_expert_ffn", "layer_forward_chunked",
+    "silu_grad", "gelu_grad", "gate_weights_backward", "layer_backward",
 ]
 
 GATE_SOFTMAX_TOPK = 0
@@ -626,6 +627,137 @@ def dispatch_volume_bytes(n_remote: int, D: int, elem_bytes: int) -> int:
 # ----------------------------------------------------------------------------------------------
 # The whole layer
 # ----------------------------------------------------------------------------------------------
+
+def silu_grad(a: np.ndarray) -> np.ndarray:
+    """d/da SiLU(a) = s(a) * (1 + a * (1 - s(a))), s the logistic sigmoid."""
+    s = 1.0 / (1.0 + np.exp(-a))
+    return s * (1.0 + a * (1.0 - s))
+
+
+def gelu_grad(a: np.ndarray) -> np.ndarray:
+    """d/da GELU(a) = Phi(a) + a * phi(a) (exact erf form)."""
+    return 0.5 * (1.0 + _erf(a / math.sqrt(2.0))) + a * np.exp(-0.5 * a * a) / math.sqrt(2.0 * math.pi)
+
+
+def gate_weights_backward(l: np.ndarray, topk_idx: np.ndarray, mode: int, dgate: np.ndarray) -> np.ndarray:
+    """Gradient of the gate values with respect to all E logits (the selection held fixed).
+
+    The chain rule through each gate definition of ``gate_weights``:
+    SOFTMAX_TOPK  g = softmax(l_sel): dl_sel = g * (dg - sum_j g_j dg_j).
+    SIGMOID_TOPK  g_j = s_j / S, s = sigmoid(l_sel), S = sum s:
+                  dl_sel_j = s_j (1 - s_j) (dg_j - sum_i g_i dg_i) / S.
+    SOFTMAX_FULL  g = p[sel], p = softmax over all E: with dp = dg scattered to
+                  the selected experts, dl = p * (dp - sum_e p_e dp_e).
+    Unselected logits get 0 except under SOFTMAX_FULL.
+    """
+    l = np.asarray(l, dtype=np.float64)
+    T, E = l.shape
+    dg = np.asarray(dgate, dtype=np.float64)
+    idx = np.asarray(topk_idx, dtype=np.int64)
+    dl = np.zeros((T, E))
+    sel = np.take_along_axis(l, idx, axis=1)
+    if mode == GATE_SOFTMAX_TOPK:
+        m = sel.max(axis=1, keepdims=True)
+        w = np.exp(sel - m)
+        g = w / w.sum(axis=1, keepdims=True)
+        dsel = g * (dg - (g * dg).sum(axis=1, keepdims=True))
+        np.put_along_axis(dl, idx, dsel, axis=1)
+    elif mode == GATE_SIGMOID_TOPK:
+        sg = 1.0 / (1.0 + np.exp(-sel))
+        S = sg.sum(axis=1, keepdims=True)
+        g = sg / S
+        dsel = sg * (1.0 - sg) * (dg - (g * dg).sum(axis=1, keepdims=True)) / S
+        np.put_along_axis(dl, idx, dsel, axis=1)
+    elif mode == GATE_SOFTMAX_FULL:
+        m = l.max(axis=1, keepdims=True)
+        w = np.exp(l - m)
+        pr = w / w.sum(axis=1, keepdims=True)
+        dp = np.zeros((T, E))
+        np.put_along_axis(dp, idx, dg, axis=1)
+        dl = pr * (dp - (pr * dp).sum(axis=1, keepdims=True))
+    else:
+        raise ValueError(f"unknown gate mode {mode}")
+    return dl
+
+
+def layer_backward(inputs: Dict, cfg, fwd: Dict, dy) -> Dict[str, np.ndarray]:
+    """Gradients of the layer output y (from ``layer_forward``) for an upstream gradient dy [T, D].
+
+    The chain rule through the forward's steps in reverse, the routing decision
+    (selection and drops) held fixed: combine -> expert FFN -> permute ->
+    router. dy_perm[row] = g * dy[t]; dgate = <dy[t], y_perm[row]>; per
+    expert dh = dy_perm W2, dW2 = dy_perm^T h; through the activation
+    (SwiGLU: da1 = dh * a3 * SiLU'(a1), da3 = dh * SiLU(a1); GELU: da1 = dh *
+    GELU'(a1)); dx_perm = da1 W1 + da3 W3, dW1 = da1^T x_perm, dW3 = da3^T
+    x_perm; dx[t] = sum of its kept rows' dx_perm + the router's dl W_g, with
+    dl from ``gate_weights_backward``; dW_g = dl^T x; dbias = sum_t dl.
+    [EPLLM] "The Execution Pipeline" (the forward steps); the backward is the
+    chain rule through them (the pages name backward only as training's other
+    half). No shared expert.
+    """
+    x = as_f64(inputs["x"])
+    T, D, E, k = cfg.T, cfg.D, cfg.E, cfg.top_k
+    dyv = as_f64(dy)
+    p2r = np.asarray(fwd["pair_to_row"], dtype=np.int64).reshape(T, k)
+    r2p = np.asarray(fwd["row_to_pair"], dtype=np.int64)
+    off = np.asarray(fwd["expert_offsets"], dtype=np.int64)
+    N = int(off[E])
+    g = np.asarray(fwd["topk_gate"], dtype=np.float64).reshape(T, k)
+    yp = np.asarray(fwd["y_perm"], dtype=np.float64)
+    xp = np.asarray(fwd["x_perm"], dtype=np.float64)
+    tok = r2p[:N] // k
+    slot = r2p[:N] % k
+    dyp = g[tok, slot][:, None] * dyv[tok]                      # [N, D]
+    dgate = np.zeros((T, k))
+    dgate[tok, slot] = (dyv[tok] * yp[:N]).sum(axis=1)
+    F = cfg.F
+    dw1 = np.zeros((E, F, D))
+    dw3 = np.zeros((E, F, D)) if cfg.act == ACT_SWIGLU else None
+    dw2 = np.zeros((E, D, F))
+    dxp = np.zeros((N, D))
+    pre1 = np.zeros((N, F))
+    pre3 = np.zeros((N, F))
+    hh = np.zeros((N, F))
+    dh_all = np.zeros((N, F))
+    da1_all = np.zeros((N, F))
+    da3_all = np.zeros((N, F))
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi <= lo:
+            continue
+        xr = xp[lo:hi]
+        w1 = as_f64(inputs["w1"][e])
+        w2 = as_f64(inputs["w2"][e])
+        a1 = xr @ w1.T
+        if cfg.act == ACT_SWIGLU:
+            w3 = as_f64(inputs["w3"][e])
+            a3 = xr @ w3.T
+            h = silu(a1) * a3
+        else:
+            a3 = None
+            h = gelu(a1)
+        dh = dyp[lo:hi] @ w2                                     # [n, F]
+        dw2[e] = dyp[lo:hi].T @ h
+        if cfg.act == ACT_SWIGLU:
+            da1 = dh * a3 * silu_grad(a1)
+            da3 = dh * silu(a1)
+            dxp[lo:hi] = da1 @ w1 + da3 @ w3
+            dw3[e] = da3.T @ xr
+            pre3[lo:hi], da3_all[lo:hi] = a3, da3
+        else:
+            da1 = dh * gelu_grad(a1)
+            dxp[lo:hi] = da1 @ w1
+        dw1[e] = da1.T @ xr
+        pre1[lo:hi], hh[lo:hi], dh_all[lo:hi], da1_all[lo:hi] = a1, h, dh, da1
+    dx = np.zeros((T, D))
+    np.add.at(dx, tok, dxp)
+    dl = gate_weights_backward(fwd["logits"], np.asarray(fwd["topk_idx"]).reshape(T, k), cfg.gate, dgate)
+    wg = as_f64(inputs["w_gate"])
+    dx = dx + dl @ wg
+    return {"dx": dx, "dw_gate": dl.T @ x, "dbias": dl.sum(axis=0), "dw1": dw1, "dw3": dw3, "dw2": dw2,
+            "dgate": dgate, "dl": dl, "dy_perm": dyp, "dh": dh_all, "da1": da1_all, "da3": da3_all,
+            "dx_perm": dxp, "a1": pre1, "a3": pre3, "h": hh}
+
 
 def shared_expert_ffn(x, w1, w3, w2, act: int) -> np.ndarray:
     """A shared expert: the same expert FFN applied to every token, with gate 1.
