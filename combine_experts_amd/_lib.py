@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
-MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS = 0, 1, 2
+MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS, MOE_STAGE_ROUTER_BWD = 0, 1, 2, 3
 
 
 class MoEError(RuntimeError):
@@ -67,6 +67,19 @@ _SIG = {
     "moe_layer_forward": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_layer_args), ctypes.c_int32, _P,
                                          _P, _P]),
     "moe_event_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
+    "moe_expert_ffn_up_train": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_transpose_weights": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_backward_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_down_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_up_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+    "moe_router_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.c_size_t, _P]),
+    "moe_backward_dx": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_wgrad_ld": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(ctypes.c_int64)]),
+    "moe_group_transpose": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
+                                           _P]),
+    "moe_expert_wgrad": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int64, _P, _P, ctypes.c_int32, _P]),
     "moe_event_destroy": (ctypes.c_int, [_P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
@@ -390,3 +403,112 @@ def moe_layer_forward(d: moe_dims, args: moe_layer_args, n_chunks: int, stream=N
     st = load_library().moe_layer_forward(ctypes.byref(d), ctypes.byref(args), int(n_chunks), _stream(stream),
                                           None if side_stream is None else _stream(side_stream), ev)
     _check("moe_layer_forward", st)
+
+
+
+# ---- backward ----------------------------------------------------------------------------------------
+
+def _nm(d):
+    return 2 if d.act == MOE_ACT_SWIGLU else 1
+
+
+def moe_expert_ffn_up_train(d: moe_dims, x_perm, expert_offsets, w1, w3, h, pre, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up_train(
+        ctypes.byref(d), _ptr(x_perm, "x_perm", dt, P * d.D), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(h, "h", dt, P * d.F), _ptr(pre, "pre", dt, P * d.F * _nm(d)), _stream(stream))
+    _check("moe_expert_ffn_up_train", st)
+
+
+def moe_transpose_weights(d: moe_dims, w1, w3, w2, w13t, w2t, stream=None) -> None:
+    dt = _elem_dtype(d)
+    n = d.E * d.F * d.D
+    st = load_library().moe_transpose_weights(
+        ctypes.byref(d), _ptr(w1, "w1", dt, n), _ptr(w3, "w3", dt, n, nullable=d.act == MOE_ACT_GELU),
+        _ptr(w2, "w2", dt, n), _ptr(w13t, "w13t", dt, n * _nm(d)), _ptr(w2t, "w2t", dt, n), _stream(stream))
+    _check("moe_transpose_weights", st)
+
+
+def moe_backward_combine(d: moe_dims, dy, pair_to_row, topk_gate, y_perm, dy_perm, dgate, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_backward_combine(
+        ctypes.byref(d), _ptr(dy, "dy", dt, d.T * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        _ptr(topk_gate, "topk_gate", torch.float32, P), _ptr(y_perm, "y_perm", dt, P * d.D),
+        _ptr(dy_perm, "dy_perm", dt, P * d.D), _ptr(dgate, "dgate", torch.float32, P), _stream(stream))
+    _check("moe_backward_combine", st)
+
+
+def moe_expert_ffn_down_backward(d: moe_dims, dy_perm, expert_offsets, w2t, pre, da, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_down_backward(
+        ctypes.byref(d), _ptr(dy_perm, "dy_perm", dt, P * d.D),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1), _ptr(w2t, "w2t", dt, d.E * d.F * d.D),
+        _ptr(pre, "pre", dt, P * d.F * _nm(d)), _ptr(da, "da", dt, P * d.F * _nm(d)), _stream(stream))
+    _check("moe_expert_ffn_down_backward", st)
+
+
+def moe_expert_ffn_up_backward(d: moe_dims, da, expert_offsets, w13t, dx_perm, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up_backward(
+        ctypes.byref(d), _ptr(da, "da", dt, P * d.F * _nm(d)),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1), _ptr(w13t, "w13t", dt, d.E * d.F * d.D * _nm(d)),
+        _ptr(dx_perm, "dx_perm", dt, P * d.D), _stream(stream))
+    _check("moe_expert_ffn_up_backward", st)
+
+
+def moe_router_backward(d: moe_dims, x, logits, topk_idx, topk_gate, dgate, dl, dw_gate, dbias=None, ws=None,
+                        stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    f32, i32 = torch.float32, torch.int32
+    st = load_library().moe_router_backward(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D, nullable=d.T == 0),
+        _ptr(logits, "logits", f32, d.T * d.E, nullable=d.T == 0), _ptr(topk_idx, "topk_idx", i32, P, nullable=d.T == 0),
+        _ptr(topk_gate, "topk_gate", f32, P, nullable=d.T == 0), _ptr(dgate, "dgate", f32, P, nullable=d.T == 0),
+        _ptr(dl, "dl", f32, d.T * d.E), _ptr(dw_gate, "dw_gate", f32, d.E * d.D),
+        _ptr(dbias, "dbias", f32, d.E, nullable=True), _ptr(ws, "ws", nullable=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_router_backward", st)
+
+
+def moe_backward_dx(d: moe_dims, dx_perm, pair_to_row, topk_idx, dl, w_gate, dx, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_backward_dx(
+        ctypes.byref(d), _ptr(dx_perm, "dx_perm", dt, P * d.D), _ptr(pair_to_row, "pair_to_row", torch.int32, P),
+        _ptr(topk_idx, "topk_idx", torch.int32, P), _ptr(dl, "dl", torch.float32, d.T * d.E),
+        _ptr(w_gate, "w_gate", dt, d.E * d.D), _ptr(dx, "dx", dt, d.T * d.D), _stream(stream))
+    _check("moe_backward_dx", st)
+
+
+def moe_wgrad_ld(d: moe_dims) -> int:
+    v = ctypes.c_int64(0)
+    _check("moe_wgrad_ld", load_library().moe_wgrad_ld(ctypes.byref(d), ctypes.byref(v)))
+    return v.value
+
+
+def moe_group_transpose(d: moe_dims, src, n_cols: int, expert_offsets, koff, dst, stream=None) -> None:
+    dt = _elem_dtype(d)
+    ld = dst.numel() // max(1, n_cols)
+    st = load_library().moe_group_transpose(
+        ctypes.byref(d), _ptr(src, "src", dt), int(n_cols), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(koff, "koff", torch.int32, d.E + 1), _ptr(dst, "dst", dt, n_cols * moe_wgrad_ld(d)), ld, _stream(stream))
+    _check("moe_group_transpose", st)
+
+
+def moe_expert_wgrad(d: moe_dims, a_t, b_t, koff, M: int, N: int, out0, out1=None, split=None, stream=None) -> None:
+    split = M if split is None else int(split)
+    ld = a_t.numel() // max(1, M)
+    if b_t.numel() // max(1, N) != ld:
+        raise ValueError("a_t and b_t must have the same row length")
+    f32 = torch.float32
+    st = load_library().moe_expert_wgrad(
+        ctypes.byref(d), _ptr(a_t, "a_t", _elem_dtype(d), M * ld), _ptr(b_t, "b_t", _elem_dtype(d), N * ld),
+        _ptr(koff, "koff", torch.int32, d.E + 1), int(M), int(N), ld, _ptr(out0, "out0", f32, d.E * split * N),
+        _ptr(out1, "out1", f32, d.E * (M - split) * N, nullable=split == M), split, _stream(stream))
+    _check("moe_expert_wgrad", st)

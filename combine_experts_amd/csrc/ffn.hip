@@ -243,10 +243,28 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, con
   }
 }
 
-template <int ACTFN, bool DUAL>
+__device__ __forceinline__ float act_silu_grad(float a) {
+  const float s = 1.f / (1.f + expf(-a));
+  return s * (1.f + a * (1.f - s));
+}
+__device__ __forceinline__ float act_gelu_grad(float a) {
+  return 0.5f * (1.f + erff(a * 0.70710678118654752f)) + a * expf(-0.5f * a * a) * 0.39894228040143268f;
+}
+
+// Epilogue modes of the bf16 grouped GEMM.
+//   EPI_PLAIN  out[r, n] = act(acc)                                     (row stride Nout)
+//   EPI_PRE    as EPI_PLAIN, and the pre-activations go to pre: SwiGLU writes W1 x to columns [0, Nout)
+//              and W3 x to [Nout, 2 Nout) of a 2*Nout-wide row; GELU writes W1 x (Nout wide)
+//   EPI_BWD    acc = dh (no activation on the way in); with a1 (and a3) read from pre as EPI_PRE wrote
+//              them: SwiGLU out[r, n] = dh*a3*SiLU'(a1), out[r, Nout + n] = dh*SiLU(a1) (2*Nout wide);
+//              GELU out[r, n] = dh*GELU'(a1) (Nout wide)
+constexpr int EPI_PLAIN = 0, EPI_PRE = 1, EPI_BWD = 2;
+
+template <int ACTFN, bool DUAL, int EPI = EPI_PLAIN>
 __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                      const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
-                                                     bf16_t* __restrict__ out, int E, int K, int Nout) {
+                                                     bf16_t* __restrict__ out, int E, int K, int Nout,
+                                                     bf16_t* __restrict__ pre) {
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
   __shared__ bf16x8 lds[2 * G_STAGE];
   const int NT = (Nout + BNO - 1) / BNO;
@@ -316,11 +334,15 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     default: gemm_kloop<1>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
+  constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
+  const int ldo = (EPI == EPI_BWD && SWI) ? 2 * Nout : Nout;   // out row stride
+  const int ldp = SWI ? 2 * Nout : Nout;                         // pre row stride
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = (2 * i + wm) * 32 + lane % 32;
     if (i >= act || r >= mrows) continue;
-    bf16_t* orow = out + (size_t)(row0 + r) * Nout + n0;
+    bf16_t* orow = out + (size_t)(row0 + r) * ldo + n0;
+    bf16_t* prow = (EPI != EPI_PLAIN) ? pre + (size_t)(row0 + r) * ldp + n0 : nullptr;
 #pragma unroll
     for (int j = 0; j < (DUAL ? 1 : 2); ++j)
 #pragma unroll
@@ -328,14 +350,118 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
         const int c = (DUAL ? wn * 32 : wn * 64 + j * 32) + 8 * q + 4 * (lane / 32);
         if (n0 + c >= Nout) continue;
         bf16x4 pk;
+        if constexpr (EPI == EPI_BWD) {
+          const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(prow + c);
+          bf16x4 pk3;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float h = acc[i][j][4 * q + u];
-          if constexpr (ACTFN == MOE_ACT_SWIGLU && DUAL) h = act_silu_fast(h) * acc[i][1][4 * q + u];
-          else if constexpr (ACTFN == MOE_ACT_GELU) h = act_gelu(h);
-          pk[u] = f2bf(h);
+          for (int u = 0; u < 4; ++u) {
+            const float dh = acc[i][j][4 * q + u], x1 = bf2f(a1[u]);
+            if constexpr (SWI) {
+              const float x3 = bf2f((*reinterpret_cast<const bf16x4*>(prow + Nout + c))[u]);
+              pk[u] = f2bf(dh * x3 * act_silu_grad(x1));
+              pk3[u] = f2bf(dh * act_silu(x1));
+            } else {
+              pk[u] = f2bf(dh * act_gelu_grad(x1));
+            }
+          }
+          *reinterpret_cast<bf16x4*>(orow + c) = pk;
+          if constexpr (SWI) *reinterpret_cast<bf16x4*>(orow + Nout + c) = pk3;
+        } else {
+          bf16x4 p1, p3;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float h = acc[i][j][4 * q + u];
+            if constexpr (EPI == EPI_PRE) {
+              p1[u] = f2bf(h);
+              if constexpr (SWI && DUAL) p3[u] = f2bf(acc[i][1][4 * q + u]);
+            }
+            if constexpr (SWI && DUAL) h = act_silu_fast(h) * acc[i][1][4 * q + u];
+            else if constexpr (ACTFN == MOE_ACT_GELU) h = act_gelu(h);
+            pk[u] = f2bf(h);
+          }
+          *reinterpret_cast<bf16x4*>(orow + c) = pk;
+          if constexpr (EPI == EPI_PRE) {
+            *reinterpret_cast<bf16x4*>(prow + c) = p1;
+            if constexpr (SWI && DUAL) *reinterpret_cast<bf16x4*>(prow + Nout + c) = p3;
+          }
         }
-        *reinterpret_cast<bf16x4*>(orow + c) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------------
+// Weight gradients: out_g = A_g^T-free form out_g[m, n] = sum_{k in group g} aT[m, k] * bT[n, k], with
+// both operands stored transposed ([M, ld] and [N, ld], the reduction index contiguous) and group g
+// owning columns [koff[g], koff[g+1]) of both, zero-padded to a multiple of 64. The k-loop is the
+// forward's; tiles are 256 x 256 of (m, n); float32 output, rows m < split to out0[g] ([split, N])
+// and the rest to out1[g] ([M - split, N]).
+// ---------------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__ aT, const bf16_t* __restrict__ bT,
+                                                      const int32_t* __restrict__ koff, int G, int M, int N,
+                                                      long long ld, float* __restrict__ out0,
+                                                      float* __restrict__ out1, int split) {
+  __shared__ bf16x8 lds[2 * G_STAGE];
+  const int MT = (M + GBM - 1) / GBM, NT = (N + GBR - 1) / GBR;
+  const int per_g = MT * NT;
+  const int t = blockIdx.x;
+  if (t >= G * per_g) return;
+  const int g = t / per_g, rem = t % per_g;
+  const int mt = rem / NT, nt = rem % NT;
+  const int m0 = mt * GBM, n0 = nt * GBR;
+  const int mrows = min(GBM, M - m0);
+  const int k0 = koff[g], nk = (koff[g + 1] - k0) / GBK;
+  const int lane = threadIdx.x % MOE_WAVE;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
+  const int wm = wave / 4, wn = wave % 4;
+  const bf16_t* src[G_LPS];
+#pragma unroll
+  for (int i = 0; i < G_LPS; ++i) {
+    const int slot = i * GTH + wave * MOE_WAVE + lane;
+    if (i * GTH < G_ACH) {
+      const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
+      src[i] = aT + (size_t)(m0 + (row < mrows ? row : 0)) * ld + k0 + ch * 8;
+    } else {
+      const int bs = slot - G_ACH;
+      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
+      src[i] = bT + (size_t)(n0 + row < N ? n0 + row : n0) * ld + k0 + ch * 8;
+    }
+  }
+  int aoff[G_KS][4], boff[G_KS][2];
+#pragma unroll
+  for (int ks = 0; ks < G_KS; ++ks) {
+    const int ch = ks * 2 + lane / 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (2 * i + wm) * 32 + lane % 32;
+      aoff[ks][i] = row * GKCH + gswz(row, ch);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = gbrow<false>(wn, j) + lane % 32;
+      boff[ks][j] = G_ACH + row * GKCH + gswz(row, ch);
+    }
+  }
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  if (nk > 0) gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk, mrows);  // uniform: an empty group writes zeros
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + (2 * i + wm) * 32 + lane % 32;
+    if (m >= M) continue;
+    float* orow = m < split ? out0 + ((size_t)g * split + m) * N : out1 + ((size_t)g * (M - split) + (m - split)) * N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = n0 + wn * 64 + j * 32 + 8 * q + 4 * (lane / 32);
+        if (c >= N) continue;
+        *reinterpret_cast<f32x4*>(orow + c) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                    acc[i][j][4 * q + 3]};
       }
   }
 }
@@ -412,22 +538,42 @@ dim3 ffn_grid(const FfnArgs& a, int tbn) {
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   if (a.n_rows_max == 0) return hipSuccess;
-  const int bno = a.act == MOE_ACT_SWIGLU ? GBR / 2 : GBR;
+  // the up-projection tile pairs W1 and W3 rows (SwiGLU forward); every other form is a plain tile
+  const bool dual = a.act == MOE_ACT_SWIGLU && a.epi != 2;
+  const int bno = dual ? GBR / 2 : GBR;
   const long long row_tiles = (a.n_rows_max + GBM - 1) / GBM + (a.E < a.n_rows_max ? a.E : a.n_rows_max);
   const dim3 grid((unsigned)(row_tiles * ((a.Nout + bno - 1) / bno) + 8));
   const bf16_t* A = (const bf16_t*)a.a;
   const bf16_t* b0 = (const bf16_t*)a.b0;
   const bf16_t* b1 = (const bf16_t*)a.b1;
   bf16_t* o = (bf16_t*)a.out;
-  if (a.act == MOE_ACT_SWIGLU)
-    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_SWIGLU, true>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o,
-                       a.E, a.K, a.Nout);
-  else if (a.act == MOE_ACT_GELU)
-    hipLaunchKernelGGL((ffn_gemm_bf16<MOE_ACT_GELU, false>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o,
-                       a.E, a.K, a.Nout);
-  else
-    hipLaunchKernelGGL((ffn_gemm_bf16<-1, false>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, a.K,
-                       a.Nout);
+  bf16_t* pr = (bf16_t*)a.pre;
+#define MOE_FFN_LAUNCH(ACTV, DUALV, EPIV)                                                                          \
+  hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, DUALV, EPIV>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, \
+                     a.K, a.Nout, pr)
+  if (a.epi == 1) {
+    if (a.act == MOE_ACT_SWIGLU) MOE_FFN_LAUNCH(MOE_ACT_SWIGLU, true, EPI_PRE);
+    else MOE_FFN_LAUNCH(MOE_ACT_GELU, false, EPI_PRE);
+  } else if (a.epi == 2) {
+    if (a.act == MOE_ACT_SWIGLU) MOE_FFN_LAUNCH(MOE_ACT_SWIGLU, false, EPI_BWD);
+    else MOE_FFN_LAUNCH(MOE_ACT_GELU, false, EPI_BWD);
+  } else if (a.act == MOE_ACT_SWIGLU) {
+    MOE_FFN_LAUNCH(MOE_ACT_SWIGLU, true, EPI_PLAIN);
+  } else if (a.act == MOE_ACT_GELU) {
+    MOE_FFN_LAUNCH(MOE_ACT_GELU, false, EPI_PLAIN);
+  } else {
+    MOE_FFN_LAUNCH(-1, false, EPI_PLAIN);
+  }
+#undef MOE_FFN_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff, int G, int M, int N, long long ld,
+                             float* out0, float* out1, int split, hipStream_t s) {
+  const long long tiles = (long long)G * ((M + GBM - 1) / GBM) * ((N + GBR - 1) / GBR);
+  if (tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(ffn_wgrad_bf16, dim3((unsigned)tiles), dim3(GTH), 0, s, (const bf16_t*)aT, (const bf16_t*)bT,
+                     koff, G, M, N, ld, out0, out1, split);
   return hipGetLastError();
 }
 

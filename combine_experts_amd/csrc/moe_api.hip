@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 103;
+constexpr int kAbiVersion = 104;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -96,6 +96,8 @@ int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes) {
     *bytes = ffn_ws_bytes(d);
   } else if (stage == MOE_STAGE_ROUTE_STATS) {
     *bytes = route_partial_rows(d) * (size_t)d->E * sizeof(float);
+  } else if (stage == MOE_STAGE_ROUTER_BWD) {
+    *bytes = moe::colsum_ws_bytes(d->T, d->E);
   } else {
     return MOE_ERR_INVALID_ARG;
   }
@@ -319,6 +321,141 @@ int moe_expert_ffn_padded_up(const moe_dims* d, const void* x_pad, const int32_t
 int moe_expert_ffn_padded_down(const moe_dims* d, const void* h_pad, const int32_t* padded_offsets, const void* w2,
                                void* y_pad, hipStream_t stream) {
   return ffn_padded(d, false, h_pad, padded_offsets, w2, nullptr, y_pad, stream);
+}
+
+// ---- backward ----------------------------------------------------------------------------------
+int moe_wgrad_ld(const moe_dims* d, int64_t* ld) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (ld == nullptr) return MOE_ERR_INVALID_ARG;
+  *ld = ((int64_t)d->T * d->top_k + 63LL * d->E + 63) / 64 * 64;
+  return MOE_OK;
+}
+
+static int ffn_bwd_common(const moe_dims* d) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;  // the training GEMM epilogues are bf16 only
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int moe_expert_ffn_up_train(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets, const void* w1,
+                            const void* w3, void* h, void* pre, hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x_perm || !expert_offsets || !w1 || !h || !pre || (d->act == MOE_ACT_SWIGLU && !w3)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(h) || !aligned16(pre) || (w3 && !aligned16(w3)))
+    return MOE_ERR_INVALID_ARG;
+  moe::FfnArgs a{x_perm, expert_offsets, w1, d->act == MOE_ACT_SWIGLU ? w3 : nullptr, h,
+                 d->T * d->top_k, d->E, d->D, d->F, d->act, 1, pre};
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
+int moe_transpose_weights(const moe_dims* d, const void* w1, const void* w3, const void* w2, void* w13t, void* w2t,
+                          hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!w1 || !w2 || !w13t || !w2t || (d->act == MOE_ACT_SWIGLU && !w3)) return MOE_ERR_INVALID_ARG;
+  const int nm = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+  const long long FD = (long long)d->F * d->D;
+  // w2t[e] [F, D] = w2[e]^T ([D, F]); w13t[e] [D, nm*F] = [w1[e]^T | w3[e]^T]
+  hipError_t e = moe::launch_transpose(w2, d->E, d->D, d->F, FD, w2t, d->D, FD, 0, d->dtype, stream);
+  if (e == hipSuccess)
+    e = moe::launch_transpose(w1, d->E, d->F, d->D, FD, w13t, (long long)nm * d->F, nm * FD, 0, d->dtype, stream);
+  if (e == hipSuccess && nm == 2)
+    e = moe::launch_transpose(w3, d->E, d->F, d->D, FD, w13t, 2LL * d->F, 2 * FD, d->F, d->dtype, stream);
+  return hip_status(e);
+}
+
+int moe_backward_combine(const moe_dims* d, const void* dy, const int32_t* pair_to_row, const float* topk_gate,
+                         const void* y_perm, void* dy_perm, float* dgate, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!dy || !pair_to_row || !topk_gate || !y_perm || !dy_perm || !dgate) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy) || !aligned16(y_perm) || !aligned16(dy_perm)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_backward_combine(dy, pair_to_row, topk_gate, y_perm, dy_perm, dgate, d->T, d->D,
+                                                 d->top_k, d->dtype, stream));
+}
+
+int moe_expert_ffn_down_backward(const moe_dims* d, const void* dy_perm, const int32_t* expert_offsets,
+                                 const void* w2t, const void* pre, void* da, hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!dy_perm || !expert_offsets || !w2t || !pre || !da) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy_perm) || !aligned16(w2t) || !aligned16(pre) || !aligned16(da)) return MOE_ERR_INVALID_ARG;
+  // dh = dy_perm W2 as A [rows, D] against w2t [F, D] per expert; the epilogue differentiates the activation
+  moe::FfnArgs a{dy_perm, expert_offsets, w2t, nullptr, da, d->T * d->top_k, d->E, d->D, d->F, d->act, 2,
+                 const_cast<void*>(pre)};
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
+int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t* expert_offsets, const void* w13t,
+                               void* dx_perm, hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!da || !expert_offsets || !w13t || !dx_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(da) || !aligned16(w13t) || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
+  const int K = (d->act == MOE_ACT_SWIGLU ? 2 : 1) * d->F;
+  moe::FfnArgs a{da, expert_offsets, w13t, nullptr, dx_perm, d->T * d->top_k, d->E, K, d->D, -1};
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
+int moe_router_backward(const moe_dims* d, const void* x, const float* logits, const int32_t* topk_idx,
+                        const float* topk_gate, const float* dgate, float* dl, float* dw_gate, float* dbias, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!dl || !dw_gate || (d->T > 0 && (!x || !logits || !topk_idx || !topk_gate || !dgate))) return MOE_ERR_INVALID_ARG;
+  if (d->top_k > 32) return MOE_ERR_UNSUPPORTED;
+  if (dbias != nullptr && (ws == nullptr || ws_bytes < moe::colsum_ws_bytes(d->T, d->E))) return MOE_ERR_WORKSPACE;
+  hipError_t e = moe::launch_router_backward(logits, topk_idx, topk_gate, dgate, dl, d->T, d->E, d->top_k, d->gate,
+                                             stream);
+  if (e == hipSuccess) e = moe::launch_tn_f32(dl, x, d->dtype, d->T, d->E, d->D, dw_gate, stream);
+  if (e == hipSuccess && dbias != nullptr) e = moe::launch_colsum(dl, d->T, d->E, static_cast<float*>(ws), dbias, stream);
+  return hip_status(e);
+}
+
+int moe_backward_dx(const moe_dims* d, const void* dx_perm, const int32_t* pair_to_row, const int32_t* topk_idx,
+                    const float* dl, const void* w_gate, void* dx, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!dx_perm || !pair_to_row || !topk_idx || !dl || !w_gate || !dx) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dx_perm) || !aligned16(w_gate) || !aligned16(dx)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_backward_dx(dx_perm, pair_to_row, topk_idx, dl, w_gate, dx, d->T, d->D, d->E,
+                                            d->top_k, d->gate == MOE_GATE_SOFTMAX_FULL, d->dtype, stream));
+}
+
+int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, const int32_t* expert_offsets,
+                        int32_t* koff, void* dst, int64_t ld, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  int64_t need = 0;
+  moe_wgrad_ld(d, &need);
+  if (n_cols < 0 || ld < need) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets || !koff || (ld > 0 && n_cols > 0 && (!src || !dst))) return MOE_ERR_INVALID_ARG;
+  hipError_t e = moe::launch_group_koff(expert_offsets, d->E, koff, stream);
+  if (e == hipSuccess) e = moe::launch_group_transpose(src, n_cols, expert_offsets, koff, d->E, ld, dst, d->dtype, stream);
+  return hip_status(e);
+}
+
+int moe_expert_wgrad(const moe_dims* d, const void* a_t, const void* b_t, const int32_t* koff, int32_t M, int32_t N,
+                     int64_t ld, float* out0, float* out1, int32_t split, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (M < 0 || N < 0 || ld < 0 || split < 0 || split > M || ld % 64 != 0) return MOE_ERR_INVALID_ARG;
+  if (!a_t || !b_t || !koff || !out0 || (split < M && !out1)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a_t) || !aligned16(b_t) || !aligned16(out0) || (out1 && !aligned16(out1))) return MOE_ERR_INVALID_ARG;
+  if (N % 4 != 0) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_wgrad_bf16(a_t, b_t, koff, d->E, M, N, ld, out0, out1, split, stream));
 }
 
 }  // extern "C"

@@ -85,6 +85,21 @@ hipError_t launch_padded_layout(const int32_t* topk_idx, const int32_t* eoff, co
 hipError_t launch_permute_padded(const void* x, const int32_t* s2p, long long n_slots, int k, int row_bytes, void* xp,
                                  hipStream_t s);
 
+hipError_t launch_backward_combine(const void* dy, const int32_t* p2r, const float* gate, const void* yp, void* dyp,
+                                   float* dgate, int T, int D, int k, int dtype, hipStream_t s);
+hipError_t launch_router_backward(const float* logits, const int32_t* idx, const float* gate, const float* dgate,
+                                  float* dl, int T, int E, int k, int mode, hipStream_t s);
+size_t colsum_ws_bytes(int rows, int cols);
+hipError_t launch_colsum(const float* m, int rows, int cols, float* part, float* out, hipStream_t s);
+hipError_t launch_tn_f32(const float* A, const void* B, int dtype, int K, int M, int N, float* C, hipStream_t s);
+hipError_t launch_backward_dx(const void* dxp, const int32_t* p2r, const int32_t* idx, const float* dl, const void* wg,
+                              void* dx, int T, int D, int E, int k, int all_experts, int dtype, hipStream_t s);
+hipError_t launch_transpose(const void* src, int B, int R, int C, long long src_batch, void* dst, long long ld_dst,
+                            long long dst_batch, int col_off, int dtype, hipStream_t s);
+hipError_t launch_group_koff(const int32_t* off, int G, int32_t* koff, hipStream_t s);
+hipError_t launch_group_transpose(const void* src, int C, const int32_t* off, const int32_t* koff, int G,
+                                  long long ld, void* dst, int dtype, hipStream_t s);
+
 struct FfnArgs {
   const void* a;              // x_perm (up) or h (down): [N_max, K]
   const int32_t* expert_offsets;
@@ -92,8 +107,12 @@ struct FfnArgs {
   const void* b1;             // W3 (up, SwiGLU) or null
   void* out;                  // h (up) or y_perm (down): [N_max, Nout]
   int32_t n_rows_max, E, K, Nout;
-  int act;                    // up: MOE_ACT_*; down: -1 (no activation)
+  int act;                    // up: MOE_ACT_*; down: -1 (no activation); epi 2: the activation to differentiate
+  int epi = 0;                // 0 plain; 1 also store pre-activations to `pre`; 2 activation backward
+  void* pre = nullptr;        // epi 1: written; epi 2: read ([N_max, 2F] SwiGLU, [N_max, F] GELU)
 };
+hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff, int G, int M, int N, long long ld,
+                             float* out0, float* out1, int split, hipStream_t s);
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s);
 

@@ -69,7 +69,8 @@ enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
 enum moe_stage {
   MOE_STAGE_LAYOUT = 0,     /* scratch of moe_dispatch_layout */
   MOE_STAGE_FFN = 1,        /* scratch of moe_expert_ffn */
-  MOE_STAGE_ROUTE_STATS = 2 /* the prob_partials buffer of moe_route_ex / moe_load_balance */
+  MOE_STAGE_ROUTE_STATS = 2, /* the prob_partials buffer of moe_route_ex / moe_load_balance */
+  MOE_STAGE_ROUTER_BWD = 3   /* scratch of moe_router_backward (column-sum partials of dbias) */
 };
 
 /* Problem statement of one layer call ([COMM] volume equation: B*S tokens as T, top-k as K,
@@ -315,6 +316,70 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
  * hipEventDestroy). */
 int moe_event_create(hipEvent_t* event);
 int moe_event_destroy(hipEvent_t event);
+
+/* ---- Backward of the one-GPU share -------------------------------------------------------------------
+ * The chain rule through the forward steps in reverse with the routing decision (selection, drops)
+ * held fixed ([EPLLM] "The Execution Pipeline" gives the forward steps; training runs them
+ * backwards). For the upstream gradient dy [T, D] of y:
+ *   dy_perm[row(t,j)] = g[t,j] dy[t]; dgate[t,j] = <dy[t], y_perm[row]>        moe_backward_combine
+ *   da = act'(a) (dy_perm W2) per expert, from the saved pre-activations a     moe_expert_ffn_down_backward
+ *   dx_perm = da [W1; W3] per expert                                           moe_expert_ffn_up_backward
+ *   dl = gate backward of dgate; dW_g = dl^T x; dbias = sum_t dl               moe_router_backward
+ *   dx[t] = sum_j dx_perm[row(t,j)] + sum_e dl[t,e] W_g[e]                     moe_backward_dx
+ *   dW2[e] = dy_perm^T h, [dW1; dW3][e] = da^T x_perm (ragged sums over rows)   moe_expert_wgrad on
+ *                                                                              moe_group_transpose'd operands
+ * The grouped GEMM steps take bf16 only (MOE_ERR_UNSUPPORTED for float32). Weight gradients are float32. */
+
+/* Forward up-projection for training: as moe_expert_ffn_up, and the pre-activations go to pre:
+ * SwiGLU pre [T*top_k, 2F] = [W1 x | W3 x], GELU pre [T*top_k, F] = W1 x (bf16, rounded once). */
+int moe_expert_ffn_up_train(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
+                            const void* w1, const void* w3, void* h, void* pre, hipStream_t stream);
+
+/* The weights as the data-gradient GEMMs read them: w2t [E, F, D] = W2^T; w13t [E, D, 2F] =
+ * [W1^T | W3^T] (SwiGLU) or [E, D, F] = W1^T (GELU). Once per weight update. */
+int moe_transpose_weights(const moe_dims* d, const void* w1, const void* w3, const void* w2, void* w13t,
+                          void* w2t, hipStream_t stream);
+
+/* dy_perm [T*top_k, D] out (rows >= N untouched); dgate [T*top_k] float32 out (0 for dropped pairs). */
+int moe_backward_combine(const moe_dims* d, const void* dy, const int32_t* pair_to_row, const float* topk_gate,
+                         const void* y_perm, void* dy_perm, float* dgate, hipStream_t stream);
+
+/* da [T*top_k, 2F] (SwiGLU: [da1 | da3]) or [T*top_k, F] (GELU) out, from dh = dy_perm W2 and pre. */
+int moe_expert_ffn_down_backward(const moe_dims* d, const void* dy_perm, const int32_t* expert_offsets,
+                                 const void* w2t, const void* pre, void* da, hipStream_t stream);
+
+/* dx_perm [T*top_k, D] out = da [W1; W3] per expert (w13t from moe_transpose_weights). */
+int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t* expert_offsets,
+                               const void* w13t, void* dx_perm, hipStream_t stream);
+
+/* Router backward: dl [T, E] float32 out (0 where a logit gets no gradient), dw_gate [E, D] float32
+ * out, dbias [E] float32 out or NULL (then ws may be NULL). logits: the forward's float32 logits;
+ * topk_gate: the forward's gates. ws: moe_workspace_size(MOE_STAGE_ROUTER_BWD) bytes.
+ * Unsupported: top_k > 32. */
+int moe_router_backward(const moe_dims* d, const void* x, const float* logits, const int32_t* topk_idx,
+                        const float* topk_gate, const float* dgate, float* dl, float* dw_gate, float* dbias,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* dx [T, D] out = sum over kept slots of dx_perm rows + sum_e dl[t,e] W_g[e] (float32 sums, one
+ * rounding). */
+int moe_backward_dx(const moe_dims* d, const void* dx_perm, const int32_t* pair_to_row, const int32_t* topk_idx,
+                    const float* dl, const void* w_gate, void* dx, hipStream_t stream);
+
+/* Columns of the transposed operands of moe_expert_wgrad: T*top_k + 63*E rounded up to 64. */
+int moe_wgrad_ld(const moe_dims* d, int64_t* ld);
+
+/* dst [n_cols, ld] = src [rows, n_cols] transposed, expert e's rows [off_e, off_e+1) going to columns
+ * [koff[e], koff[e] + count_e) and zeros up to koff[e+1] = koff[e] + roundup64(count_e);
+ * koff [E+1] int32 out. ld >= moe_wgrad_ld(). */
+int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, const int32_t* expert_offsets,
+                        int32_t* koff, void* dst, int64_t ld, hipStream_t stream);
+
+/* Per expert e: out_e[m, n] = sum over columns [koff[e], koff[e+1]) of a_t[m, col] * b_t[n, col]
+ * (a_t [M, ld], b_t [N, ld] bf16, as moe_group_transpose writes them); rows m < split go to
+ * out0 [E, split, N], the rest to out1 [E, M - split, N] (float32). dW2 = wgrad(dy_perm^T, h^T,
+ * M = D, N = F); [dW1; dW3] = wgrad(da^T, x_perm^T, M = 2F (or F), N = D, split = F). */
+int moe_expert_wgrad(const moe_dims* d, const void* a_t, const void* b_t, const int32_t* koff, int32_t M,
+                     int32_t N, int64_t ld, float* out0, float* out1, int32_t split, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_str(int status);

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 103
+    assert M.moe_abi_version() == 104
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -206,3 +206,25 @@ def test_layer_forward_host_checks():
     a.layout_ws, a.layout_ws_bytes = 256, 1 << 20
     a.shared_w1, a.shared_F = 256, 64
     assert lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(a), 2, None, None, None) == M.MOE_ERR_INVALID_ARG
+
+
+def test_backward_host_checks():
+    lib = M.load_library()
+    fake = ctypes.c_void_p(256)
+    d32 = M.make_dims(16, 64, 8, 2, 64, dtype=M.MOE_F32)
+    # the training GEMMs are bf16 only
+    assert lib.moe_expert_ffn_up_train(ctypes.byref(d32), fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_down_backward(ctypes.byref(d32), fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_UNSUPPORTED
+    d = M.make_dims(16, 64, 8, 2, 64)
+    # the padded column count of the transposed wgrad operands
+    assert M.moe_wgrad_ld(d) == (16 * 2 + 63 * 8 + 63) // 64 * 64
+    # a too-short transposed buffer, and a split past M
+    assert lib.moe_group_transpose(ctypes.byref(d), fake, 64, fake, fake, fake, 64, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_wgrad(ctypes.byref(d), fake, fake, fake, 64, 64, 576, fake, fake, 65, None) == \
+        M.MOE_ERR_INVALID_ARG
+    # dbias without its workspace
+    assert lib.moe_router_backward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, None) == \
+        M.MOE_ERR_WORKSPACE
+    assert M.moe_workspace_size(d, M.MOE_STAGE_ROUTER_BWD) == 1 * 8 * 4

@@ -1,0 +1,236 @@
+"""GPU parity of the layer backward (bf16), stage by stage against the oracle.
+
+Each GPU step is compared with the oracle's formula for that step applied to the GPU's own inputs
+for it (the saved forward tensors and the previous backward step's output), so integer routing
+differences never enter: dy_perm and dgate, the activation backward da, dx_perm, the router's dl,
+dW_g and dbias, the final dx, the transposes (bit for bit) and the three weight gradients. dx is also
+compared end to end with the oracle's float64 layer backward on decisive tokens.
+Tolerances: bf16 outputs 2e-2 per row relative to the row's largest reference entry (one bf16
+rounding of an fp32 sum is 2^-9, the operands carry one rounding each); float32 outputs
+(dgate, dl, dW_g, dbias, weight gradients) 1e-3 relative to the largest reference entry.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_experts_amd as M
+import oracle as O
+import workloads as W
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+TOL_ROW = 2e-2
+TOL_F32 = 1e-3
+
+CASES = {
+    "mixtral_small": W.get_config("mixtral", T=512, D=512, F=448),
+    "dsv3_small": W.get_config("dsv3", T=320, D=512, F=320),
+    "gelu_k1_bias": W.MoEConfig(name="gelu_k1_bias", T=384, D=256, E=16, top_k=1, F=512, act=W.ACT_GELU, ep_size=4,
+                                bias="normal0.5", seed=61),
+    "full_softmax": W.MoEConfig(name="full_softmax", T=256, D=128, E=8, top_k=3, F=192, gate=W.GATE_SOFTMAX_FULL,
+                                bias="normal0.5", seed=62),
+    "capacity": W.MoEConfig(name="capacity", T=400, D=128, E=6, top_k=2, F=128, capacity_factor=0.8, seed=63),
+    "skew_small": W.get_config("skew", T=1024, D=256, F=192),
+}
+
+
+def _nm(cfg):
+    return 2 if cfg.act == W.ACT_SWIGLU else 1
+
+
+def _rel(got, ref):
+    return P.rel_err_rows(np.asarray(got, dtype=np.float64).reshape(len(ref), -1), np.asarray(ref).reshape(len(ref), -1))
+
+
+def _scaled(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    return np.abs(np.asarray(got, dtype=np.float64) - ref).max() / max(np.abs(ref).max(), 1e-30)
+
+
+def _train_forward(cfg, inp):
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device="cuda", logits=True)
+    P_ = cfg.T * cfg.top_k
+    pre = torch.empty((P_, _nm(cfg) * cfg.F), dtype=torch.bfloat16, device="cuda")
+    M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, buf.logits)
+    M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts, buf.rank_offsets,
+                          buf.pair_to_row, buf.row_to_pair, buf.layout_ws)
+    M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm)
+    M.moe_expert_ffn_up_train(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], buf.h, pre)
+    M.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm)
+    M.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y)
+    return d, buf, pre
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_stages(name):
+    cfg = CASES[name]
+    print(f"[backward] {name}: {cfg}", flush=True)
+    T, D, E, k, F = cfg.T, cfg.D, cfg.E, cfg.top_k, cfg.F
+    nm = _nm(cfg)
+    inp = W.make_inputs(cfg, "cuda")
+    host = P.to_host(inp)
+    d, buf, pre = _train_forward(cfg, inp)
+    torch.cuda.synchronize()
+    # the training forward's h equals the plain forward's, and pre holds the GEMM pre-activations
+    h_plain = torch.empty_like(buf.h)
+    M.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], h_plain)
+    torch.cuda.synchronize()
+    N = int(buf.expert_offsets[-1])
+    assert torch.equal(h_plain[:N], buf.h[:N]), "h of the training forward"
+    off = P.i64(buf.expert_offsets)
+    xp = P.f64(buf.x_perm[:N])
+    experts = np.searchsorted(off, np.arange(N), side="right") - 1
+    a1_ref = np.zeros((N, F))
+    a3_ref = np.zeros((N, F))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            a1_ref[lo:hi] = xp[lo:hi] @ O.as_f64(host["w1"][e]).T
+            if nm == 2:
+                a3_ref[lo:hi] = xp[lo:hi] @ O.as_f64(host["w3"][e]).T
+    pre_h = P.f64(pre[:N])
+    assert _rel(pre_h[:, :F], a1_ref).max() <= TOL_ROW, "pre-activation W1 x"
+    if nm == 2:
+        assert _rel(pre_h[:, F:], a3_ref).max() <= TOL_ROW, "pre-activation W3 x"
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    dy = torch.randn((T, D), generator=g, device="cuda").to(torch.bfloat16)
+    dyh = P.f64(dy)
+    Pn = T * k
+    dy_perm = torch.empty((Pn, D), dtype=torch.bfloat16, device="cuda")
+    dgate = torch.empty(Pn, dtype=torch.float32, device="cuda")
+    M.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm, dy_perm, dgate)
+    w13t = torch.empty((E, D, nm * F), dtype=torch.bfloat16, device="cuda")
+    w2t = torch.empty((E, F, D), dtype=torch.bfloat16, device="cuda")
+    M.moe_transpose_weights(d, inp["w1"], inp["w3"], inp["w2"], w13t, w2t)
+    da = torch.empty((Pn, nm * F), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_down_backward(d, dy_perm, buf.expert_offsets, w2t, pre, da)
+    dx_perm = torch.empty((Pn, D), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_up_backward(d, da, buf.expert_offsets, w13t, dx_perm)
+    dl = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    dwg = torch.empty((E, D), dtype=torch.float32, device="cuda")
+    dbias = torch.empty(E, dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_ROUTER_BWD), dtype=torch.uint8, device="cuda")
+    M.moe_router_backward(d, inp["x"], buf.logits, buf.topk_idx, buf.topk_gate, dgate, dl, dwg, dbias, ws)
+    dx = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
+    M.moe_backward_dx(d, dx_perm, buf.pair_to_row, buf.topk_idx, dl, inp["w_gate"], dx)
+    torch.cuda.synchronize()
+
+    # weight transposes: bit for bit
+    assert torch.equal(w2t, inp["w2"].transpose(1, 2))
+    assert torch.equal(w13t[:, :, :F], inp["w1"].transpose(1, 2))
+    if nm == 2:
+        assert torch.equal(w13t[:, :, F:], inp["w3"].transpose(1, 2))
+
+    # dy_perm, dgate on the GPU's saved tensors
+    p2r = P.i64(buf.pair_to_row)
+    r2p = P.i64(buf.row_to_pair)[:N]
+    gates = P.f64(buf.topk_gate)
+    tok = r2p // k
+    dyp_ref = gates[r2p][:, None] * dyh[tok]
+    assert _rel(P.f64(dy_perm[:N]), dyp_ref).max() <= TOL_ROW, "dy_perm"
+    yp = P.f64(buf.y_perm[:N])
+    dgate_ref = np.zeros(Pn)
+    dgate_ref[r2p] = (dyh[tok] * yp).sum(axis=1)
+    scale = (np.abs(dyh[tok]) * np.abs(yp)).sum(axis=1)
+    dg = P.f64(dgate)
+    assert np.all(np.abs(dg[r2p] - dgate_ref[r2p]) <= 1e-5 * scale + 1e-30), "dgate"
+    assert np.all(dg[p2r < 0] == 0), "dgate of dropped pairs"
+
+    # da from the GPU's dy_perm and pre
+    dyp_h = P.f64(dy_perm[:N])
+    dh = np.zeros((N, F))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            dh[lo:hi] = dyp_h[lo:hi] @ O.as_f64(host["w2"][e])
+    a1 = pre_h[:, :F]
+    if nm == 2:
+        a3 = pre_h[:, F:]
+        da_ref = np.concatenate([dh * a3 * O.silu_grad(a1), dh * O.silu(a1)], axis=1)
+    else:
+        da_ref = dh * O.gelu_grad(a1)
+    assert _rel(P.f64(da[:N]), da_ref).max() <= TOL_ROW, "da (activation backward)"
+
+    # dx_perm from the GPU's da
+    da_h = P.f64(da[:N])
+    dxp_ref = np.zeros((N, D))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi > lo:
+            dxp_ref[lo:hi] = da_h[lo:hi, :F] @ O.as_f64(host["w1"][e])
+            if nm == 2:
+                dxp_ref[lo:hi] += da_h[lo:hi, F:] @ O.as_f64(host["w3"][e])
+    assert _rel(P.f64(dx_perm[:N]), dxp_ref).max() <= TOL_ROW, "dx_perm"
+
+    # router: dl from the GPU's logits, selection, gates... and dgate
+    l_gpu = P.f64(buf.logits).reshape(T, E)
+    idx = P.i64(buf.topk_idx).reshape(T, k)
+    dl_ref = O.gate_weights_backward(l_gpu, idx, cfg.gate, dg.reshape(T, k))
+    assert _scaled(P.f64(dl), dl_ref) <= TOL_F32, "dl"
+    dl_h = P.f64(dl)
+    xh = O.as_f64(host["x"])
+    assert _scaled(P.f64(dwg), dl_h.T @ xh) <= TOL_F32, "dW_g"
+    assert _scaled(P.f64(dbias), dl_h.sum(axis=0)) <= TOL_F32, "dbias"
+
+    # dx from the GPU's dx_perm and dl
+    dxp_h = P.f64(dx_perm[:N])
+    dx_ref = np.zeros((T, D))
+    np.add.at(dx_ref, tok, dxp_h)
+    dx_ref += dl_h @ O.as_f64(host["w_gate"])
+    assert _rel(P.f64(dx), dx_ref).max() <= TOL_ROW, "dx"
+
+    # transposes of the wgrad operands: bit for bit against torch, zero padding between groups
+    ld = M.moe_wgrad_ld(d)
+    koff = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    tr = {}
+    for key, src, C in (("dyp", dy_perm, D), ("h", buf.h, F), ("da", da, nm * F), ("xp", buf.x_perm, D)):
+        dst = torch.full((C, ld), 7.0, dtype=torch.bfloat16, device="cuda")
+        M.moe_group_transpose(d, src, C, buf.expert_offsets, koff, dst)
+        tr[key] = dst
+    torch.cuda.synchronize()
+    kh = P.i64(koff)
+    assert kh[0] == 0 and np.all(np.diff(kh) == (np.diff(off) + 63) // 64 * 64)
+    for key, src, C in (("dyp", dy_perm, D), ("h", buf.h, F), ("da", da, nm * F), ("xp", buf.x_perm, D)):
+        for e in range(E):
+            lo, hi = int(off[e]), int(off[e + 1])
+            got = tr[key][:, kh[e]:kh[e + 1]]
+            assert torch.equal(got[:, :hi - lo], src[lo:hi].t()), f"transpose {key} expert {e}"
+            assert bool((got[:, hi - lo:] == 0).all()), f"padding {key} expert {e}"
+
+    # weight gradients
+    dw2 = torch.empty((E, D, F), dtype=torch.float32, device="cuda")
+    M.moe_expert_wgrad(d, tr["dyp"], tr["h"], koff, D, F, dw2)
+    dw1 = torch.empty((E, F, D), dtype=torch.float32, device="cuda")
+    dw3 = torch.empty((E, F, D), dtype=torch.float32, device="cuda") if nm == 2 else None
+    M.moe_expert_wgrad(d, tr["da"], tr["xp"], koff, nm * F, D, dw1, dw3, split=F)
+    torch.cuda.synchronize()
+    h_h = P.f64(buf.h[:N])
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        ref2 = dyp_h[lo:hi].T @ h_h[lo:hi]
+        ref1 = da_h[lo:hi, :F].T @ xp[lo:hi]
+        if hi == lo:
+            assert bool((dw2[e] == 0).all()) and bool((dw1[e] == 0).all()), f"expert {e} without rows"
+            continue
+        assert _scaled(P.f64(dw2[e]), ref2) <= TOL_F32, f"dW2 expert {e}"
+        assert _scaled(P.f64(dw1[e]), ref1) <= TOL_F32, f"dW1 expert {e}"
+        if nm == 2:
+            assert _scaled(P.f64(dw3[e]), da_h[lo:hi, F:].T @ xp[lo:hi]) <= TOL_F32, f"dW3 expert {e}"
+
+    # end to end: dx against the oracle's float64 backward on decisive tokens (dropless only)
+    if cfg.capacity_factor <= 0:
+        fwd = O.layer_forward(host, cfg)
+        bwd = O.layer_backward(host, cfg, fwd, dyh)
+        dec = O.decisive_tokens(fwd["logits"], k, 1e-3, cfg.n_groups, cfg.topk_groups, cfg.gate)["order"]
+        same = (fwd["topk_idx"] == idx).all(axis=1) & dec
+        assert same.mean() > 0.5
+        err = P.rel_err_rows(P.f64(dx)[same], bwd["dx"][same])
+        assert err.max() <= 5e-2, f"dx end to end: max rel err {err.max():.3e}"
+        print(f"[backward] {name}: dx end-to-end max rel err {err.max():.2e} on {same.sum()} tokens", flush=True)
