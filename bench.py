@@ -204,6 +204,68 @@ def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
     return out
 
 
+def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
+    """One training step's backward at the workload shape, stage by stage (HIP events on the stream)."""
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device="cuda", logits=True)
+    bw = M.BackwardBuffers(d, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    dy = torch.randn((cfg.T, cfg.D), generator=g, device="cuda").to(torch.bfloat16)
+    nm = 2 if cfg.act == W.ACT_SWIGLU else 1
+    x, w1, w3, w2 = inp["x"], inp["w1"], inp["w3"], inp["w2"]
+    stages = [
+        ("transpose_weights", lambda: M.moe_transpose_weights(d, w1, w3, w2, bw.w13t, bw.w2t, stream)),
+        ("backward_combine", lambda: M.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm,
+                                                            bw.dy_perm, bw.dgate, stream)),
+        ("dgrad_down_act", lambda: M.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre,
+                                                                  bw.da, stream)),
+        ("dgrad_up", lambda: M.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)),
+        ("router_backward", lambda: M.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate,
+                                                          bw.dl, bw.dw_gate, bw.dbias, bw.router_ws, stream)),
+        ("backward_dx", lambda: M.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, inp["w_gate"],
+                                                  bw.dx, stream)),
+        ("transpose_dy_h", lambda: (M.moe_group_transpose(d, bw.dy_perm, d.D, buf.expert_offsets, bw.koff, bw.dyp_t,
+                                                          stream),
+                                    M.moe_group_transpose(d, buf.h, d.F, buf.expert_offsets, bw.koff, bw.h_t, stream))),
+        ("wgrad_w2", lambda: M.moe_expert_wgrad(d, bw.dyp_t, bw.h_t, bw.koff, d.D, d.F, bw.dw2, stream=stream)),
+        ("transpose_da_x", lambda: (M.moe_group_transpose(d, bw.da, nm * d.F, buf.expert_offsets, bw.koff, bw.da_t,
+                                                          stream),
+                                    M.moe_group_transpose(d, buf.x_perm, d.D, buf.expert_offsets, bw.koff, bw.xp_t,
+                                                          stream))),
+        ("wgrad_w13", lambda: M.moe_expert_wgrad(d, bw.da_t, bw.xp_t, bw.koff, nm * d.F, d.D, bw.dw1, bw.dw3,
+                                                 split=d.F, stream=stream)),
+    ]
+    fwd = lambda: M.forward_train(buf, bw, x, inp["w_gate"], inp["bias"], w1, w3, w2, stream)
+    fwd()
+    for _, f in stages:
+        f()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 2)] for _ in range(reps)]
+    for r in range(reps):
+        ev[r][0].record(stream)
+        fwd()
+        ev[r][1].record(stream)
+        for i, (_, f) in enumerate(stages):
+            f()
+            ev[r][i + 2].record(stream)
+    torch.cuda.synchronize()
+    st = {name: sum(ev[r][i + 1].elapsed_time(ev[r][i + 2]) for r in range(reps)) / reps
+          for i, (name, _) in enumerate(stages)}
+    fwd_ms = sum(ev[r][0].elapsed_time(ev[r][1]) for r in range(reps)) / reps
+    N = int(buf.expert_offsets[-1].item())
+    gemm_flops = 2.0 * N * cfg.D * cfg.F * (1 + nm + 1 + nm)
+    gemm_ms = st["dgrad_down_act"] + st["dgrad_up"] + st["wgrad_w2"] + st["wgrad_w13"]
+    total = sum(v for k_, v in st.items() if k_ != "transpose_weights")
+    out = {"stage_ms": {k_: round(v, 4) for k_, v in st.items()}, "total_ms": round(total, 4),
+           "forward_train_ms": round(fwd_ms, 4), "train_step_ms": round(fwd_ms + total, 4),
+           "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
+           "train_tokens_per_s": round(cfg.T / ((fwd_ms + total) * 1e-3), 1)}
+    del buf, bw, dy
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -336,6 +398,7 @@ def main(argv=None):
     cluster = measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b)
     padded = measure_padded(M, W, torch, cfg, inp, stream, time_calls)
     overlap = measure_overlap(M, W, torch, cfg, inp, stream, time_calls)
+    bwd = measure_backward(M, W, torch, cfg, inp, stream) if cfg.dtype == W.DT_BF16 else None
     extra_ms.update({"dispatch_matrix": cluster["dispatch_matrix_ms"], "recv_layout": cluster["recv_layout_ms"],
                      "exchange_gather": cluster["exchange_gather_ms"], "return_scatter": cluster["return_scatter_ms"]})
     for s_, v in extra_ms.items():
@@ -349,6 +412,12 @@ def main(argv=None):
         f"{overlap['overlapped_ms']:.3f} ms; with a shared expert (F={overlap['shared_F']}) "
         f"{overlap['shared_sequential_ms']:.3f} / {overlap['shared_overlapped_ms']:.3f} ms, shared expert beside the "
         f"routed FFN on one batch {overlap['shared_concurrent_ms']:.3f} ms")
+    if bwd is not None:
+        log(f"[bench] backward {bwd['total_ms']:.3f} ms (+ weight transposes {bwd['stage_ms']['transpose_weights']:.3f} ms "
+            f"once per update); grouped GEMMs {bwd['gemm_tflops']:.0f} TFLOP/s; training step (forward with saved "
+            f"pre-activations + backward) {bwd['train_step_ms']:.3f} ms")
+        for s_, v in bwd["stage_ms"].items():
+            log(f"[bench]     bwd {s_:20s} {v * 1e3:9.1f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -371,6 +440,7 @@ def main(argv=None):
         "cluster_emulation": cluster,
         "padded_capacity": padded,
         "overlap": overlap,
+        "backward": bwd,
         "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
         "gemm_mfma_frac": round(ffn_tflops / peak, 4),
         "roofline": roofline,

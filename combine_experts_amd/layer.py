@@ -113,3 +113,72 @@ class LayerExecutor:
             a.shared_h, a.shared_y, a.shared_offsets = p(self.shared_h), p(self.shared_y), p(self.shared_offsets)
         L.moe_layer_forward(self.d, a, self.n_chunks, stream, self.side, self.events)
         return self.y
+
+
+class BackwardBuffers:
+    """Buffers of one training step's backward for dims d (bf16): saved pre-activations, transposed
+    weights, the backward's activations, transposed wgrad operands and float32 gradients."""
+
+    def __init__(self, d: L.moe_dims, device="cuda"):
+        self.d = d
+        dt = torch.bfloat16
+        P, E, D, F = d.T * d.top_k, d.E, d.D, d.F
+        nm = 2 if d.act == L.MOE_ACT_SWIGLU else 1
+        f32 = dict(dtype=torch.float32, device=device)
+        self.pre = torch.empty((P, nm * F), dtype=dt, device=device)
+        self.w13t = torch.empty((E, D, nm * F), dtype=dt, device=device)
+        self.w2t = torch.empty((E, F, D), dtype=dt, device=device)
+        self.dy_perm = torch.empty((P, D), dtype=dt, device=device)
+        self.dgate = torch.empty(P, **f32)
+        self.da = torch.empty((P, nm * F), dtype=dt, device=device)
+        self.dx_perm = torch.empty((P, D), dtype=dt, device=device)
+        self.dl = torch.empty((d.T, E), **f32)
+        self.dw_gate = torch.empty((E, D), **f32)
+        self.dbias = torch.empty(E, **f32)
+        self.router_ws = torch.empty(max(1, L.moe_workspace_size(d, L.MOE_STAGE_ROUTER_BWD)), dtype=torch.uint8,
+                                     device=device)
+        self.dx = torch.empty((d.T, D), dtype=dt, device=device)
+        ld = L.moe_wgrad_ld(d)
+        self.koff = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.dyp_t = torch.empty((D, ld), dtype=dt, device=device)
+        self.h_t = torch.empty((F, ld), dtype=dt, device=device)
+        self.da_t = torch.empty((nm * F, ld), dtype=dt, device=device)
+        self.xp_t = torch.empty((D, ld), dtype=dt, device=device)
+        self.dw1 = torch.empty((E, F, D), **f32)
+        self.dw3 = torch.empty((E, F, D), **f32) if nm == 2 else None
+        self.dw2 = torch.empty((E, D, F), **f32)
+
+
+def forward_train(buf: MoELayerBuffers, bw: BackwardBuffers, x, w_gate, bias, w1, w3, w2, stream=None):
+    """The forward with what the backward needs saved: logits (buf must hold them) and pre-activations."""
+    d = buf.d
+    L.moe_route(d, x, w_gate, bias, buf.topk_idx, buf.topk_gate, buf.logits, stream)
+    L.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
+                          buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
+    L.moe_permute(d, x, buf.pair_to_row, buf.x_perm, stream)
+    L.moe_expert_ffn_up_train(d, buf.x_perm, buf.expert_offsets, w1, w3, buf.h, bw.pre, stream)
+    L.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, w2, buf.y_perm, stream)
+    L.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
+    return buf.y
+
+
+def backward(buf: MoELayerBuffers, bw: BackwardBuffers, x, w_gate, dy, stream=None, transpose_weights=None):
+    """The backward steps in order (``transpose_weights``: (w1, w3, w2) to refresh bw.w13t / bw.w2t first,
+    as after a weight update). Gradients land in bw.dx, bw.dw_gate, bw.dbias, bw.dw1, bw.dw3, bw.dw2."""
+    d = buf.d
+    nm = 2 if d.act == L.MOE_ACT_SWIGLU else 1
+    if transpose_weights is not None:
+        L.moe_transpose_weights(d, *transpose_weights, bw.w13t, bw.w2t, stream)
+    L.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm, bw.dy_perm, bw.dgate, stream)
+    L.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre, bw.da, stream)
+    L.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)
+    L.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate, bw.dl, bw.dw_gate, bw.dbias,
+                          bw.router_ws, stream)
+    L.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, w_gate, bw.dx, stream)
+    L.moe_group_transpose(d, bw.dy_perm, d.D, buf.expert_offsets, bw.koff, bw.dyp_t, stream)
+    L.moe_group_transpose(d, buf.h, d.F, buf.expert_offsets, bw.koff, bw.h_t, stream)
+    L.moe_expert_wgrad(d, bw.dyp_t, bw.h_t, bw.koff, d.D, d.F, bw.dw2, stream=stream)
+    L.moe_group_transpose(d, bw.da, nm * d.F, buf.expert_offsets, bw.koff, bw.da_t, stream)
+    L.moe_group_transpose(d, buf.x_perm, d.D, buf.expert_offsets, bw.koff, bw.xp_t, stream)
+    L.moe_expert_wgrad(d, bw.da_t, bw.xp_t, bw.koff, nm * d.F, d.D, bw.dw1, bw.dw3, split=d.F, stream=stream)
+    return bw.dx
