@@ -222,7 +222,9 @@ def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
                                                                   bw.da, stream)),
         ("dgrad_up", lambda: M.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)),
         ("router_backward", lambda: M.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate,
-                                                          bw.dl, bw.dw_gate, bw.dbias, bw.router_ws, stream)),
+                                                          bw.dl, bw.dw_gate, bw.dbias, bw.router_ws, stream,
+                                                          all_expert_offsets=buf.expert_offsets,
+                                                          all_row_to_pair=buf.row_to_pair)),
         ("backward_dx", lambda: M.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, inp["w_gate"],
                                                   bw.dx, stream)),
         ("transpose_dy_h", lambda: (M.moe_group_transpose(d, bw.dy_perm, d.D, buf.expert_offsets, bw.koff, bw.dyp_t,

@@ -72,7 +72,7 @@ _SIG = {
     "moe_backward_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_down_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_up_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
-    "moe_router_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "moe_router_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_backward_dx": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_wgrad_ld": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(ctypes.c_int64)]),
@@ -462,7 +462,7 @@ def moe_expert_ffn_up_backward(d: moe_dims, da, expert_offsets, w13t, dx_perm, s
 
 
 def moe_router_backward(d: moe_dims, x, logits, topk_idx, topk_gate, dgate, dl, dw_gate, dbias=None, ws=None,
-                        stream=None) -> None:
+                        stream=None, all_expert_offsets=None, all_row_to_pair=None) -> None:
     dt = _elem_dtype(d)
     P = d.T * d.top_k
     f32, i32 = torch.float32, torch.int32
@@ -470,6 +470,8 @@ def moe_router_backward(d: moe_dims, x, logits, topk_idx, topk_gate, dgate, dl, 
         ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D, nullable=d.T == 0),
         _ptr(logits, "logits", f32, d.T * d.E, nullable=d.T == 0), _ptr(topk_idx, "topk_idx", i32, P, nullable=d.T == 0),
         _ptr(topk_gate, "topk_gate", f32, P, nullable=d.T == 0), _ptr(dgate, "dgate", f32, P, nullable=d.T == 0),
+        _ptr(all_expert_offsets, "all_expert_offsets", i32, d.E + 1, nullable=True),
+        _ptr(all_row_to_pair, "all_row_to_pair", i32, P, nullable=True),
         _ptr(dl, "dl", f32, d.T * d.E), _ptr(dw_gate, "dw_gate", f32, d.E * d.D),
         _ptr(dbias, "dbias", f32, d.E, nullable=True), _ptr(ws, "ws", nullable=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))

@@ -191,6 +191,43 @@ __global__ void __launch_bounds__(256) tn_f32_kernel(const float* __restrict__ A
     }
 }
 
+// dW_g[e] = sum over the pairs (t, j) that selected e of dl[t, e] x[t], grouped by expert: rows
+// [off[e], off[e+1]) of a dropless layout list those pairs (row_to_pair). Block (e, d-chunk of 64*VN
+// columns); 4 waves split the rows round robin and are added in wave order: deterministic.
+template <typename T>
+__global__ void __launch_bounds__(256) router_wgrad_grouped_kernel(const T* __restrict__ x, const float* __restrict__ dl,
+                                                                   const int32_t* __restrict__ off,
+                                                                   const int32_t* __restrict__ r2p, int E, int D, int k,
+                                                                   float* __restrict__ dwg) {
+  constexpr int VN = 16 / sizeof(T);
+  const int e = blockIdx.x;
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  const int c = blockIdx.y * MOE_WAVE + lane;  // 16-byte chunk of the row
+  const int nch = D / VN;
+  __shared__ float part[4][MOE_WAVE * VN];
+  float acc[VN];
+#pragma unroll
+  for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+  const int lo = off[e], hi = off[e + 1];
+  if (c < nch) {
+    for (int r = lo + wave; r < hi; r += 4) {
+      const int t = r2p[r] / k;
+      const float w = dl[(size_t)t * E + e];
+      const u32x4 raw = reinterpret_cast<const u32x4*>(x + (size_t)t * D)[c];
+      const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int i = 0; i < VN; ++i) acc[i] = fmaf(w, ld_f32(v + i), acc[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < VN; ++i) part[wave][lane * VN + i] = acc[i];
+  __syncthreads();
+  for (int q = threadIdx.x; q < MOE_WAVE * VN; q += blockDim.x) {
+    const int col = blockIdx.y * MOE_WAVE * VN + q;
+    if (col < D) dwg[(size_t)e * D + col] = ((part[0][q] + part[1][q]) + part[2][q]) + part[3][q];
+  }
+}
+
 // dx[t] = sum over kept slots of dx_perm[row] + sum_e dl[t, e] W_g[e] (the selected experts, or all E
 // under full-softmax gates), float32 sums in slot / expert order, one rounding. One wave per token,
 // 16-byte chunks.
@@ -235,24 +272,38 @@ __global__ void __launch_bounds__(256) backward_dx_kernel(const T* __restrict__ 
 }
 
 // Batched transpose through 64 x 64 LDS tiles: dst[b][c][col_off + r] = src[b][r][c] (dst rows of
-// ld_dst elements), for r < R, c < C.
+// ld_dst elements), for r < R, c < C. Global reads and writes move 16 bytes per lane; the tile is
+// transposed on its way into LDS ([c][r] rows padded by one 16-byte chunk). Requires C % VN == 0.
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_kernel(const T* __restrict__ src, int R, int C, long long src_batch,
                                                         T* __restrict__ dst, long long ld_dst, long long dst_batch,
                                                         int col_off) {
-  __shared__ T tile[64][65];
+  constexpr int VN = 16 / sizeof(T), CPR = 64 / VN;  // elements per chunk, chunks per 64-wide row
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + VN];
   const int b = blockIdx.z, r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const T* s = src + b * src_batch;
   T* d = dst + b * dst_batch;
-  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-  for (int i = ty; i < 64; i += 4) {
-    const int r = r0 + i, c = c0 + tx;
-    if (r < R && c < C) tile[i][tx] = s[(size_t)r * C + c];
+  const int tid = threadIdx.x;
+  for (int q = tid; q < 64 * CPR; q += 256) {
+    const int rl = q / CPR, cc = q % CPR;
+    const int r = r0 + rl, c = c0 + cc * VN;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (r < R && c < C) raw = *reinterpret_cast<const u32x4*>(s + (size_t)r * C + c);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) tile[cc * VN + i][rl] = v[i];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i, r = r0 + tx;
-    if (r < R && c < C) d[(size_t)c * ld_dst + col_off + r] = tile[tx][i];
+  for (int q = tid; q < 64 * CPR; q += 256) {
+    const int cl = q / CPR, rc = q % CPR;
+    const int c = c0 + cl, r = r0 + rc * VN;
+    if (c >= C || r >= R) continue;
+    T* out = d + (size_t)c * ld_dst + col_off + r;
+    if (r + VN <= R && ((col_off + r) % VN) == 0 && (ld_dst % VN) == 0) {
+      *reinterpret_cast<u32x4*>(out) = *reinterpret_cast<const u32x4*>(&tile[cl][rc * VN]);
+    } else {
+      for (int i = 0; i < VN && r + i < R; ++i) out[i] = tile[cl][rc * VN + i];
+    }
   }
 }
 
@@ -270,13 +321,15 @@ __global__ void __launch_bounds__(256) group_koff_kernel(const int32_t* __restri
 }
 
 // dst[c][koff[g] + j] = src[off[g] + j][c] for j < count_g, 0 for count_g <= j < padded count;
-// 64-column tiles of the padded axis (each inside one group) x 64-row tiles of c.
+// 64-column tiles of the padded axis (each inside one group, as the padded groups are 64-aligned) x
+// 64-row tiles of c, 16-byte global reads and writes. Requires C % VN == 0.
 template <typename T>
 __global__ void __launch_bounds__(256) group_transpose_kernel(const T* __restrict__ src, int C,
                                                               const int32_t* __restrict__ off,
                                                               const int32_t* __restrict__ koff, int G,
                                                               T* __restrict__ dst, long long ld) {
-  __shared__ T tile[64][65];
+  constexpr int VN = 16 / sizeof(T), CPR = 64 / VN;
+  __shared__ __attribute__((aligned(16))) T tile[64][64 + VN];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
   const int total = koff[G];
   if (j0 >= total) return;
@@ -288,15 +341,22 @@ __global__ void __launch_bounds__(256) group_transpose_kernel(const T* __restric
   const int g = a;
   const int cnt = off[g + 1] - off[g], base = off[g] + (j0 - koff[g]);
   const int valid = cnt - (j0 - koff[g]);  // rows of this tile that exist (may be <= 0)
-  const int tx = threadIdx.x % 64, ty = threadIdx.x / 64;
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + tx;
-    tile[i][tx] = (i < valid && c < C) ? src[(size_t)(base + i) * C + c] : st_cvt<T>(0.f);
+  const int tid = threadIdx.x;
+  for (int q = tid; q < 64 * CPR; q += 256) {
+    const int jl = q / CPR, cc = q % CPR;
+    const int c = c0 + cc * VN;
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (jl < valid && c < C) raw = *reinterpret_cast<const u32x4*>(src + (size_t)(base + jl) * C + c);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) tile[cc * VN + i][jl] = v[i];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) {
-    const int c = c0 + i;
-    if (c < C) dst[(size_t)c * ld + j0 + tx] = tile[tx][i];
+  for (int q = tid; q < 64 * CPR; q += 256) {
+    const int cl = q / CPR, jc = q % CPR;
+    const int c = c0 + cl;
+    if (c < C)
+      *reinterpret_cast<u32x4*>(dst + (size_t)c * ld + j0 + jc * VN) = *reinterpret_cast<const u32x4*>(&tile[cl][jc * VN]);
   }
 }
 
@@ -346,6 +406,19 @@ hipError_t launch_tn_f32(const float* A, const void* B, int dtype, int K, int M,
     hipLaunchKernelGGL(tn_f32_kernel<bf16_t>, grid, dim3(256), 0, s, A, (const bf16_t*)B, K, M, N, C);
   else
     hipLaunchKernelGGL(tn_f32_kernel<float>, grid, dim3(256), 0, s, A, (const float*)B, K, M, N, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad_grouped(const void* x, const float* dl, const int32_t* off, const int32_t* r2p, int E,
+                                       int D, int k, int dtype, float* dwg, hipStream_t s) {
+  const int VN = dtype == MOE_BF16 ? 8 : 4;
+  const dim3 grid(E, (D / VN + MOE_WAVE - 1) / MOE_WAVE);
+  if (dtype == MOE_BF16)
+    hipLaunchKernelGGL(router_wgrad_grouped_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, dl, off, r2p, E, D,
+                       k, dwg);
+  else
+    hipLaunchKernelGGL(router_wgrad_grouped_kernel<float>, grid, dim3(256), 0, s, (const float*)x, dl, off, r2p, E, D, k,
+                       dwg);
   return hipGetLastError();
 }
 

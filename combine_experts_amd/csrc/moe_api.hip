@@ -358,6 +358,7 @@ int moe_transpose_weights(const moe_dims* d, const void* w1, const void* w3, con
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (!w1 || !w2 || !w13t || !w2t || (d->act == MOE_ACT_SWIGLU && !w3)) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, d->D) || !row_vec_ok(d, d->F)) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   const int nm = d->act == MOE_ACT_SWIGLU ? 2 : 1;
   const long long FD = (long long)d->F * d->D;
   // w2t[e] [F, D] = w2[e]^T ([D, F]); w13t[e] [D, nm*F] = [w1[e]^T | w3[e]^T]
@@ -407,16 +408,27 @@ int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t*
 }
 
 int moe_router_backward(const moe_dims* d, const void* x, const float* logits, const int32_t* topk_idx,
-                        const float* topk_gate, const float* dgate, float* dl, float* dw_gate, float* dbias, void* ws,
+                        const float* topk_gate, const float* dgate, const int32_t* all_expert_offsets,
+                        const int32_t* all_row_to_pair, float* dl, float* dw_gate, float* dbias, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (!dl || !dw_gate || (d->T > 0 && (!x || !logits || !topk_idx || !topk_gate || !dgate))) return MOE_ERR_INVALID_ARG;
+  if ((all_expert_offsets == nullptr) != (all_row_to_pair == nullptr)) return MOE_ERR_INVALID_ARG;
   if (d->top_k > 32) return MOE_ERR_UNSUPPORTED;
+  if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
   if (dbias != nullptr && (ws == nullptr || ws_bytes < moe::colsum_ws_bytes(d->T, d->E))) return MOE_ERR_WORKSPACE;
   hipError_t e = moe::launch_router_backward(logits, topk_idx, topk_gate, dgate, dl, d->T, d->E, d->top_k, d->gate,
                                              stream);
-  if (e == hipSuccess) e = moe::launch_tn_f32(dl, x, d->dtype, d->T, d->E, d->D, dw_gate, stream);
+  // dW_g = dl^T x: only the selected experts' columns of dl are nonzero under top-k gates, so with a
+  // dropless grouping of the pairs the product is a per-expert weighted row sum; dense otherwise
+  if (e == hipSuccess) {
+    if (all_expert_offsets != nullptr && d->gate != MOE_GATE_SOFTMAX_FULL)
+      e = moe::launch_router_wgrad_grouped(x, dl, all_expert_offsets, all_row_to_pair, d->E, d->D, d->top_k, d->dtype,
+                                           dw_gate, stream);
+    else
+      e = moe::launch_tn_f32(dl, x, d->dtype, d->T, d->E, d->D, dw_gate, stream);
+  }
   if (e == hipSuccess && dbias != nullptr) e = moe::launch_colsum(dl, d->T, d->E, static_cast<float*>(ws), dbias, stream);
   return hip_status(e);
 }
@@ -441,6 +453,7 @@ int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, cons
   moe_wgrad_ld(d, &need);
   if (n_cols < 0 || ld < need) return MOE_ERR_INVALID_ARG;
   if (!expert_offsets || !koff || (ld > 0 && n_cols > 0 && (!src || !dst))) return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, n_cols)) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   hipError_t e = moe::launch_group_koff(expert_offsets, d->E, koff, stream);
   if (e == hipSuccess) e = moe::launch_group_transpose(src, n_cols, expert_offsets, koff, d->E, ld, dst, d->dtype, stream);
   return hip_status(e);

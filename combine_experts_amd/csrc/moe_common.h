@@ -92,6 +92,8 @@ hipError_t launch_router_backward(const float* logits, const int32_t* idx, const
 size_t colsum_ws_bytes(int rows, int cols);
 hipError_t launch_colsum(const float* m, int rows, int cols, float* part, float* out, hipStream_t s);
 hipError_t launch_tn_f32(const float* A, const void* B, int dtype, int K, int M, int N, float* C, hipStream_t s);
+hipError_t launch_router_wgrad_grouped(const void* x, const float* dl, const int32_t* off, const int32_t* r2p, int E,
+                                       int D, int k, int dtype, float* dwg, hipStream_t s);
 hipError_t launch_backward_dx(const void* dxp, const int32_t* p2r, const int32_t* idx, const float* dl, const void* wg,
                               void* dx, int T, int D, int E, int k, int all_experts, int dtype, hipStream_t s);
 hipError_t launch_transpose(const void* src, int B, int R, int C, long long src_batch, void* dst, long long ld_dst,

@@ -172,8 +172,11 @@ def backward(buf: MoELayerBuffers, bw: BackwardBuffers, x, w_gate, dy, stream=No
     L.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm, bw.dy_perm, bw.dgate, stream)
     L.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre, bw.da, stream)
     L.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)
+    grouped = {}
+    if d.capacity_factor <= 0:  # the forward's layout is dropless: dW_g grouped by expert
+        grouped = dict(all_expert_offsets=buf.expert_offsets, all_row_to_pair=buf.row_to_pair)
     L.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate, bw.dl, bw.dw_gate, bw.dbias,
-                          bw.router_ws, stream)
+                          bw.router_ws, stream, **grouped)
     L.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, w_gate, bw.dx, stream)
     L.moe_group_transpose(d, bw.dy_perm, d.D, buf.expert_offsets, bw.koff, bw.dyp_t, stream)
     L.moe_group_transpose(d, buf.h, d.F, buf.expert_offsets, bw.koff, bw.h_t, stream)

@@ -355,10 +355,14 @@ int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t*
 /* Router backward: dl [T, E] float32 out (0 where a logit gets no gradient), dw_gate [E, D] float32
  * out, dbias [E] float32 out or NULL (then ws may be NULL). logits: the forward's float32 logits;
  * topk_gate: the forward's gates. ws: moe_workspace_size(MOE_STAGE_ROUTER_BWD) bytes.
- * Unsupported: top_k > 32. */
+ * all_expert_offsets / all_row_to_pair: a dropless layout of topk_idx (moe_dispatch_layout with
+ * capacity_factor <= 0; for a dropless layer the forward's own) -- then dW_g is summed per expert
+ * over the pairs that selected it (k of E columns of dl are nonzero); NULL for both: dense dl^T x
+ * (always so under MOE_GATE_SOFTMAX_FULL). Unsupported: top_k > 32. */
 int moe_router_backward(const moe_dims* d, const void* x, const float* logits, const int32_t* topk_idx,
-                        const float* topk_gate, const float* dgate, float* dl, float* dw_gate, float* dbias,
-                        void* ws, size_t ws_bytes, hipStream_t stream);
+                        const float* topk_gate, const float* dgate, const int32_t* all_expert_offsets,
+                        const int32_t* all_row_to_pair, float* dl, float* dw_gate, float* dbias, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 /* dx [T, D] out = sum over kept slots of dx_perm rows + sum_e dl[t,e] W_g[e] (float32 sums, one
  * rounding). */

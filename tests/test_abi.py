@@ -225,6 +225,9 @@ def test_backward_host_checks():
     assert lib.moe_expert_wgrad(ctypes.byref(d), fake, fake, fake, 64, 64, 576, fake, fake, 65, None) == \
         M.MOE_ERR_INVALID_ARG
     # dbias without its workspace
-    assert lib.moe_router_backward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, None) == \
-        M.MOE_ERR_WORKSPACE
+    assert lib.moe_router_backward(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, fake, fake, fake, None, 0,
+                                   None) == M.MOE_ERR_WORKSPACE
+    # the grouped form needs both arrays of the dropless layout
+    assert lib.moe_router_backward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, fake, fake, None, None, 0,
+                                   None) == M.MOE_ERR_INVALID_ARG
     assert M.moe_workspace_size(d, M.MOE_STAGE_ROUTER_BWD) == 1 * 8 * 4

@@ -118,6 +118,19 @@ def test_backward_stages(name):
     dbias = torch.empty(E, dtype=torch.float32, device="cuda")
     ws = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_ROUTER_BWD), dtype=torch.uint8, device="cuda")
     M.moe_router_backward(d, inp["x"], buf.logits, buf.topk_idx, buf.topk_gate, dgate, dl, dwg, dbias, ws)
+    # the expert-grouped dW_g, on a dropless layout of the same selection (the forward's own when dropless)
+    if cfg.capacity_factor > 0:
+        dd = M.dims_from_config(cfg.replace(capacity_factor=0.0))
+        lb = M.MoELayerBuffers(dd, device="cuda")
+        M.moe_dispatch_layout(dd, buf.topk_idx, lb.expert_counts, lb.expert_offsets, lb.rank_counts, lb.rank_offsets,
+                              lb.pair_to_row, lb.row_to_pair, lb.layout_ws)
+        all_off, all_r2p = lb.expert_offsets, lb.row_to_pair
+    else:
+        all_off, all_r2p = buf.expert_offsets, buf.row_to_pair
+    dl2 = torch.empty_like(dl)
+    dwg2 = torch.empty_like(dwg)
+    M.moe_router_backward(d, inp["x"], buf.logits, buf.topk_idx, buf.topk_gate, dgate, dl2, dwg2, None, None,
+                          all_expert_offsets=all_off, all_row_to_pair=all_r2p)
     dx = torch.empty((T, D), dtype=torch.bfloat16, device="cuda")
     M.moe_backward_dx(d, dx_perm, buf.pair_to_row, buf.topk_idx, dl, inp["w_gate"], dx)
     torch.cuda.synchronize()
@@ -177,6 +190,8 @@ def test_backward_stages(name):
     dl_h = P.f64(dl)
     xh = O.as_f64(host["x"])
     assert _scaled(P.f64(dwg), dl_h.T @ xh) <= TOL_F32, "dW_g"
+    assert torch.equal(dl2, dl), "dl does not depend on the dW_g form"
+    assert _scaled(P.f64(dwg2), dl_h.T @ xh) <= TOL_F32, "dW_g grouped by expert"
     assert _scaled(P.f64(dbias), dl_h.sum(axis=0)) <= TOL_F32, "dbias"
 
     # dx from the GPU's dx_perm and dl
