@@ -275,6 +275,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the forward step (no load-balancing, cluster, padded, executor or backward "
+                         "measurements), e.g. under a profiler")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--copy-calib-bytes", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many bytes 3 times (a plain copy kernel "
@@ -371,55 +374,57 @@ def main(argv=None):
     log(f"[bench] permute {permute_gbs:.0f} GB/s, combine {combine_gbs:.0f} GB/s, "
         f"FFN {ffn_tflops:.0f} TFLOP/s ({ffn_tflops / peak * 100:.1f}% of peak)")
 
-    # Stages beyond the forward step, timed on their own after it (not part of `value`):
-    # load balancing = the router with a selection-only bias and probability sums, then the
-    # statistics / bias-step kernel.
-    def time_calls(fn, reps=20):
-        fn()
-        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
+    extra_ms, cluster, padded, overlap, bwd = {}, None, None, None, None
+    if not args.no_extras:
+        # Stages beyond the forward step, timed on their own after it (not part of `value`):
+        # load balancing = the router with a selection-only bias and probability sums, then the
+        # statistics / bias-step kernel.
+        def time_calls(fn, reps=20):
             fn()
-        z.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(z) / reps
+            a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(reps):
+                fn()
+            z.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(z) / reps
 
-    sb = W.make_select_bias(cfg, dev)
-    part = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_ROUTE_STATS) // 4, dtype=torch.float32, device=dev)
-    stats = torch.empty(2 * cfg.E + 2, dtype=torch.float32, device=dev)
-    extra_ms = {
-        "route_ex": time_calls(lambda: M.moe_route_ex(d, inp["x"], inp["w_gate"], inp["bias"], sb, buf.topk_idx,
-                                                      buf.topk_gate, None, part, stream)),
-        "load_balance": time_calls(lambda: M.moe_load_balance(d, buf.expert_counts, part, 0.01, stats, 0.0, None,
-                                                              stream)),
-    }
-    # the routing the step left in buf is restored before the cluster and padded measurements
-    M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, None, stream)
-    M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
-                          buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
-    cluster = measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b)
-    padded = measure_padded(M, W, torch, cfg, inp, stream, time_calls)
-    overlap = measure_overlap(M, W, torch, cfg, inp, stream, time_calls)
-    bwd = measure_backward(M, W, torch, cfg, inp, stream) if cfg.dtype == W.DT_BF16 else None
-    extra_ms.update({"dispatch_matrix": cluster["dispatch_matrix_ms"], "recv_layout": cluster["recv_layout_ms"],
-                     "exchange_gather": cluster["exchange_gather_ms"], "return_scatter": cluster["return_scatter_ms"]})
-    for s_, v in extra_ms.items():
-        log(f"[bench]   {s_:15s} {v * 1e3:9.1f} us (outside the step)")
-    log(f"[bench] emulated exchange over {cluster['n_src']} sources: {cluster['rows']} rows, gather "
-        f"{cluster['exchange_gbps']:.0f} GB/s, scatter {cluster['return_gbps']:.0f} GB/s")
-    log(f"[bench] padded layout at CF {padded['capacity_factor']}: C={padded['C']}, padding "
-        f"{padded['padding_frac']:.1%}, dropped {padded['dropped']}; compact path {padded['compact_ms']:.3f} ms, "
-        f"padded path {padded['padded_ms']:.3f} ms")
-    log(f"[bench] executor: 1 stream {overlap['sequential_ms']:.3f} ms, {overlap['n_chunks']} micro-batches on 2 streams "
-        f"{overlap['overlapped_ms']:.3f} ms; with a shared expert (F={overlap['shared_F']}) "
-        f"{overlap['shared_sequential_ms']:.3f} / {overlap['shared_overlapped_ms']:.3f} ms, shared expert beside the "
-        f"routed FFN on one batch {overlap['shared_concurrent_ms']:.3f} ms")
-    if bwd is not None:
-        log(f"[bench] backward {bwd['total_ms']:.3f} ms (+ weight transposes {bwd['stage_ms']['transpose_weights']:.3f} ms "
-            f"once per update); grouped GEMMs {bwd['gemm_tflops']:.0f} TFLOP/s; training step (forward with saved "
-            f"pre-activations + backward) {bwd['train_step_ms']:.3f} ms")
-        for s_, v in bwd["stage_ms"].items():
-            log(f"[bench]     bwd {s_:20s} {v * 1e3:9.1f} us")
+        sb = W.make_select_bias(cfg, dev)
+        part = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_ROUTE_STATS) // 4, dtype=torch.float32, device=dev)
+        stats = torch.empty(2 * cfg.E + 2, dtype=torch.float32, device=dev)
+        extra_ms = {
+            "route_ex": time_calls(lambda: M.moe_route_ex(d, inp["x"], inp["w_gate"], inp["bias"], sb, buf.topk_idx,
+                                                          buf.topk_gate, None, part, stream)),
+            "load_balance": time_calls(lambda: M.moe_load_balance(d, buf.expert_counts, part, 0.01, stats, 0.0, None,
+                                                                  stream)),
+        }
+        # the routing the step left in buf is restored before the cluster and padded measurements
+        M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], buf.topk_idx, buf.topk_gate, None, stream)
+        M.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
+                              buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
+        cluster = measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b)
+        padded = measure_padded(M, W, torch, cfg, inp, stream, time_calls)
+        overlap = measure_overlap(M, W, torch, cfg, inp, stream, time_calls)
+        bwd = measure_backward(M, W, torch, cfg, inp, stream) if cfg.dtype == W.DT_BF16 else None
+        extra_ms.update({"dispatch_matrix": cluster["dispatch_matrix_ms"], "recv_layout": cluster["recv_layout_ms"],
+                         "exchange_gather": cluster["exchange_gather_ms"], "return_scatter": cluster["return_scatter_ms"]})
+        for s_, v in extra_ms.items():
+            log(f"[bench]   {s_:15s} {v * 1e3:9.1f} us (outside the step)")
+        log(f"[bench] emulated exchange over {cluster['n_src']} sources: {cluster['rows']} rows, gather "
+            f"{cluster['exchange_gbps']:.0f} GB/s, scatter {cluster['return_gbps']:.0f} GB/s")
+        log(f"[bench] padded layout at CF {padded['capacity_factor']}: C={padded['C']}, padding "
+            f"{padded['padding_frac']:.1%}, dropped {padded['dropped']}; compact path {padded['compact_ms']:.3f} ms, "
+            f"padded path {padded['padded_ms']:.3f} ms")
+        log(f"[bench] executor: 1 stream {overlap['sequential_ms']:.3f} ms, {overlap['n_chunks']} micro-batches on 2 streams "
+            f"{overlap['overlapped_ms']:.3f} ms; with a shared expert (F={overlap['shared_F']}) "
+            f"{overlap['shared_sequential_ms']:.3f} / {overlap['shared_overlapped_ms']:.3f} ms, shared expert beside the "
+            f"routed FFN on one batch {overlap['shared_concurrent_ms']:.3f} ms")
+        if bwd is not None:
+            log(f"[bench] backward {bwd['total_ms']:.3f} ms (+ weight transposes {bwd['stage_ms']['transpose_weights']:.3f} ms "
+                f"once per update); grouped GEMMs {bwd['gemm_tflops']:.0f} TFLOP/s; training step (forward with saved "
+                f"pre-activations + backward) {bwd['train_step_ms']:.3f} ms")
+            for s_, v in bwd["stage_ms"].items():
+                log(f"[bench]     bwd {s_:20s} {v * 1e3:9.1f} us")
 
     cpu = None
     if not args.no_cpu_baseline:
