@@ -83,14 +83,16 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // ---------------------------------------------------------------------------------------------------
 // bf16 grouped GEMM on matrix cores.
 //
-// Block: 8 waves (2 per SIMD) own a 256-row x 256-B-row tile; for SwiGLU the 256 B rows are 128
-// rows of W1 and the matching 128 rows of W3, so the block produces 256 x 128 of h. Wave (wm, wn)
+// Block: 8 waves (2 per SIMD) own a 320-row x 256-B-row tile; for SwiGLU the 256 B rows are 128
+// rows of W1 and the matching 128 rows of W3, so the block produces 320 x 128 of h. Wave (wm, wn)
 // holds m-blocks {2i + wm} (32 rows each, interleaved so a ragged tile splits evenly between the
-// two wave rows) against 2 B blocks of 32 rows: 8 v_mfma_f32_32x32x16_bf16 per 16-deep k-step,
-// accumulators 4 x 2 x 16 floats. The weight fragment is the MFMA's first operand, so each lane
+// two wave rows) against 2 B blocks of 32 rows: 10 v_mfma_f32_32x32x16_bf16 per 16-deep k-step,
+// accumulators 5 x 2 x 16 floats (255 VGPRs, no spills). 320 rows rather than 256: an expert with
+// 2*256 + a few rows, common when routing is near even, needs two tiles instead of three, and every
+// tile re-streams the expert's weights. The weight fragment is the MFMA's first operand, so each lane
 // ends up with 4 consecutive output columns of one token row: 8-byte stores in the epilogue.
 //
-// K runs in 64-deep stages through a 2-slot LDS ring (64 KB per slot). Loads go straight from
+// K runs in 64-deep stages through a 2-slot LDS ring (72 KB per slot). Loads go straight from
 // global memory into LDS (16 bytes per lane, no register staging); a whole stage is issued at once,
 // one stage ahead, at the start of the stage before it. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
 // ch ^ ((row >> 1) & 7), so the 32 rows one fragment read touches fall on distinct banks.
@@ -103,7 +105,8 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // values) and never stored; 32-row blocks entirely past the count are not multiplied.
 // ---------------------------------------------------------------------------------------------------
 constexpr int GW = 8, GTH = GW * MOE_WAVE;        // waves / threads per block
-constexpr int GBM = 256, GBR = 256, GBK = 64;      // tile rows, B rows per tile, K per stage
+constexpr int GBM = 320, GBR = 256, GBK = 64;      // tile rows, B rows per tile, K per stage
+constexpr int GMB = GBM / 64;                       // 32-row blocks per wave (two wave rows)
 constexpr int GKCH = GBK / 8;                       // 16-byte chunks per tile row
 constexpr int G_ACH = GBM * GKCH, G_STAGE = (GBM + GBR) * GKCH, G_LPS = G_STAGE / GTH, G_KS = GBK / 16;
 constexpr int G_GN = 8;                             // column tiles per group in the tile order
@@ -191,8 +194,8 @@ __device__ __forceinline__ int gbrow(int wn, int j) {
 }
 
 template <int ACT>  // active 32-row blocks of this wave
-__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
-                                           const int (&aoff)[G_KS][4], const int (&boff)[G_KS][2], int wave, int nk,
+__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
+                                           const int (&aoff)[G_KS][GMB], const int (&boff)[G_KS][2], int wave, int nk,
                                            int mrows) {
   // load i fills tile rows [i*64, i*64+64) of A (i < G_ACH/GTH) or a part of B; A loads wholly past
   // the tile's rows are skipped (those rows feed only accumulators that are never stored)
@@ -202,7 +205,7 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[4][2], bf16x8* lds, con
                                      (__attribute__((address_space(3))) void*)(lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE),
                                      16, 0, 0);
   };
-  bf16x8 fa[2][4], fb[2][2];
+  bf16x8 fa[2][GMB], fb[2][2];
   auto frag = [&](int buf, int ks, int r) {
     const bf16x8* s = lds + buf * G_STAGE;
 #pragma unroll
@@ -301,12 +304,12 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
       src[i] = p + ch * 8;
     }
   }
-  int aoff[G_KS][4], boff[G_KS][2];
+  int aoff[G_KS][GMB], boff[G_KS][2];
 #pragma unroll
   for (int ks = 0; ks < G_KS; ++ks) {
     const int ch = ks * 2 + lane / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < GMB; ++i) {
       const int row = (2 * i + wm) * 32 + lane % 32;
       aoff[ks][i] = row * GKCH + gswz(row, ch);
     }
@@ -318,9 +321,9 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   }
   const int nblk = (mrows + 31) / 32;
   const int act = __builtin_amdgcn_readfirstlane((nblk - wm + 1) / 2);  // blocks 2i+wm < nblk
-  f32x16 acc[4][2];
+  f32x16 acc[GMB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < GMB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -328,6 +331,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
+    case 5: gemm_kloop<5>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
     case 4: gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
     case 3: gemm_kloop<3>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
     case 2: gemm_kloop<2>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
@@ -338,7 +342,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int ldo = (EPI == EPI_BWD && SWI) ? 2 * Nout : Nout;   // out row stride
   const int ldp = SWI ? 2 * Nout : Nout;                         // pre row stride
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < GMB; ++i) {
     const int r = (2 * i + wm) * 32 + lane % 32;
     if (i >= act || r >= mrows) continue;
     bf16_t* orow = out + (size_t)(row0 + r) * ldo + n0;
@@ -426,12 +430,12 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
       src[i] = bT + (size_t)(n0 + row < N ? n0 + row : n0) * ld + k0 + ch * 8;
     }
   }
-  int aoff[G_KS][4], boff[G_KS][2];
+  int aoff[G_KS][GMB], boff[G_KS][2];
 #pragma unroll
   for (int ks = 0; ks < G_KS; ++ks) {
     const int ch = ks * 2 + lane / 32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < GMB; ++i) {
       const int row = (2 * i + wm) * 32 + lane % 32;
       aoff[ks][i] = row * GKCH + gswz(row, ch);
     }
@@ -441,16 +445,16 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
       boff[ks][j] = G_ACH + row * GKCH + gswz(row, ch);
     }
   }
-  f32x16 acc[4][2];
+  f32x16 acc[GMB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < GMB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk, mrows);  // uniform: an empty group writes zeros
+  if (nk > 0) gemm_kloop<GMB>(acc, lds, src, aoff, boff, wave, nk, mrows);  // uniform: an empty group writes zeros
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < GMB; ++i) {
     const int m = m0 + (2 * i + wm) * 32 + lane % 32;
     if (m >= M) continue;
     float* orow = m < split ? out0 + ((size_t)g * split + m) * N : out1 + ((size_t)g * (M - split) + (m - split)) * N;
