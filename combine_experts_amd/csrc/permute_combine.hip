@@ -112,6 +112,67 @@ __global__ void __launch_bounds__(256) combine_kernel(const T* __restrict__ yp, 
   }
 }
 
+// Combine for k <= KMAX: the token's rows and gates are read once; for each group of U chunks per lane
+// all k rows' loads are issued before the first FMA, so k*U 16-byte loads are in flight per lane
+// (the k rows of a token sit in unrelated places of y_perm). Same slot-order float32 sums as
+// combine_kernel, so the same bits.
+template <typename T, bool ADD, int KMAX, int U>
+__global__ void __launch_bounds__(256) combine_k_kernel(const T* __restrict__ yp, const int32_t* __restrict__ p2r,
+                                                        const float* __restrict__ gate, const T* __restrict__ add,
+                                                        T* __restrict__ y, int T_, int D, int k) {
+  constexpr int VN = Vec<T>::N;
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  const int row_chunks = D / VN;
+  for (int t = blockIdx.x * kWaves + wave; t < T_; t += gridDim.x * kWaves) {
+    int rows[KMAX];
+    float g[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? p2r[(size_t)t * k + j] : -1;
+      g[j] = j < k ? gate[(size_t)t * k + j] : 0.f;
+    }
+    for (int c0 = 0; c0 < row_chunks; c0 += MOE_WAVE * U) {
+      u32x4 raw[KMAX][U];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          raw[j][u] = (rows[j] >= 0 && c < row_chunks)
+                          ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(yp + (size_t)rows[j] * D) + c)
+                          : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        float acc[VN];
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (rows[j] < 0) continue;
+          const T* e = reinterpret_cast<const T*>(&raw[j][u]);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[i] = fmaf(g[j], to_f32<T>(e[i]), acc[i]);
+        }
+        if (c < row_chunks) {
+          if constexpr (ADD) {
+            const u32x4 ra = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(add + (size_t)t * D) + c);
+            const T* e = reinterpret_cast<const T*>(&ra);
+#pragma unroll
+            for (int i = 0; i < VN; ++i) acc[i] += to_f32<T>(e[i]);
+          }
+          u32x4 o;
+          T* oe = reinterpret_cast<T*>(&o);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) oe[i] = from_f32<T>(acc[i]);
+          __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(y + (size_t)t * D) + c);
+        }
+      }
+    }
+  }
+}
+
 int grid_for(int T) {
   const int blocks = (T + kWaves - 1) / kWaves;
   return blocks < 65535 * 4 ? blocks : 65535 * 4;
@@ -129,9 +190,26 @@ hipError_t launch_permute(const void* x, const int32_t* pair_to_row, void* x_per
   return hipGetLastError();
 }
 
+template <typename T, bool ADD>
+bool launch_combine_k(const void* y_perm, const int32_t* pair_to_row, const float* gate, const void* add, void* y,
+                      int32_t T_, int32_t D, int32_t k, hipStream_t s) {
+#define MOE_COMBINE_K(KM, UU)                                                                                       \
+  hipLaunchKernelGGL((combine_k_kernel<T, ADD, KM, UU>), dim3(grid_for(T_)), dim3(256), 0, s, (const T*)y_perm,    \
+                     pair_to_row, gate, (const T*)add, (T*)y, T_, D, k)
+  if (k <= 2) MOE_COMBINE_K(2, 4);
+  else if (k <= 4) MOE_COMBINE_K(4, 2);
+  else if (k <= 8) MOE_COMBINE_K(8, 2);
+  else return false;
+#undef MOE_COMBINE_K
+  return true;
+}
+
 template <typename T>
 void launch_combine_t(const void* y_perm, const int32_t* pair_to_row, const float* gate, const void* add, void* y,
                       int32_t T_, int32_t D, int32_t k, hipStream_t s) {
+  if (add != nullptr ? launch_combine_k<T, true>(y_perm, pair_to_row, gate, add, y, T_, D, k, s)
+                     : launch_combine_k<T, false>(y_perm, pair_to_row, gate, add, y, T_, D, k, s))
+    return;
   if (add != nullptr)
     hipLaunchKernelGGL((combine_kernel<T, true>), dim3(grid_for(T_)), dim3(256), 0, s, (const T*)y_perm, pair_to_row,
                        gate, (const T*)add, (T*)y, T_, D, k);
