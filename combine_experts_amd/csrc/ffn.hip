@@ -100,7 +100,7 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // Tile order: a block's tile comes from its index through an XCD-aware map (workgroups are handed
 // to the 8 XCDs round robin): XCD x takes a contiguous range of the expert-major tile list, so
 // the tiles of one expert run together on one XCD and share its L2 (each x_perm row and weight
-// row is fetched from HBM about once). Within an expert, tiles go in groups of 8 column tiles,
+// row is fetched from HBM about once). Within an expert, tiles go in groups of 4 column tiles,
 // row-tile-major inside a group. Rows past the expert's count are loaded from row 0 (finite
 // values) and never stored; 32-row blocks entirely past the count are not multiplied.
 // ---------------------------------------------------------------------------------------------------
@@ -109,7 +109,7 @@ constexpr int GBM = 320, GBR = 256, GBK = 64;      // tile rows, B rows per tile
 constexpr int GMB = GBM / 64;                       // 32-row blocks per wave (two wave rows)
 constexpr int GKCH = GBK / 8;                       // 16-byte chunks per tile row
 constexpr int G_ACH = GBM * GKCH, G_STAGE = (GBM + GBR) * GKCH, G_LPS = G_STAGE / GTH, G_KS = GBK / 16;
-constexpr int G_GN = 8;                             // column tiles per group in the tile order
+constexpr int G_GN = 4;                             // column tiles per group in the tile order
 
 __device__ __forceinline__ int gswz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
 
