@@ -45,7 +45,17 @@ class moe_layer_args(ctypes.Structure):
                                   "expert_offsets", "rank_counts", "rank_offsets", "layout_ws")] + \
         [("layout_ws_bytes", ctypes.c_size_t)] + \
         [(n, _P) for n in ("shared_w1", "shared_w3", "shared_w2")] + [("shared_F", ctypes.c_int32)] + \
-        [(n, _P) for n in ("shared_h", "shared_y", "shared_offsets")]
+        [(n, _P) for n in ("shared_h", "shared_y", "shared_offsets", "logits", "pre")]
+
+
+class moe_backward_args(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("x", "w_gate", "w1", "w3", "w2", "logits", "topk_idx", "topk_gate",
+                                  "expert_offsets", "pair_to_row", "row_to_pair", "x_perm", "h", "pre", "y_perm",
+                                  "dy", "w13t", "w2t")] + [("refresh_weights", ctypes.c_int32)] + \
+        [(n, _P) for n in ("dy_perm", "dgate", "da", "dx_perm", "dl", "router_ws")] + \
+        [("router_ws_bytes", ctypes.c_size_t), ("koff", _P)] + \
+        [(n, _P) for n in ("dy_perm_t", "h_t", "da_t", "x_perm_t")] + [("ld", ctypes.c_int64)] + \
+        [(n, _P) for n in ("dx", "dw_gate", "dbias", "dw1", "dw3", "dw2")]
 _SIG = {
     "moe_abi_version": (ctypes.c_int, []),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
@@ -81,6 +91,7 @@ _SIG = {
     "moe_expert_wgrad": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int64, _P, _P, ctypes.c_int32, _P]),
     "moe_event_destroy": (ctypes.c_int, [_P]),
+    "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_backward_args), _P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
@@ -514,3 +525,8 @@ def moe_expert_wgrad(d: moe_dims, a_t, b_t, koff, M: int, N: int, out0, out1=Non
         _ptr(koff, "koff", torch.int32, d.E + 1), int(M), int(N), ld, _ptr(out0, "out0", f32, d.E * split * N),
         _ptr(out1, "out1", f32, d.E * (M - split) * N, nullable=split == M), split, _stream(stream))
     _check("moe_expert_wgrad", st)
+
+
+def moe_layer_backward(d: moe_dims, args: moe_backward_args, stream=None) -> None:
+    """Marshalling only: ``args`` is filled by ``layer.backward`` from its torch buffers."""
+    _check("moe_layer_backward", load_library().moe_layer_backward(ctypes.byref(d), ctypes.byref(args), _stream(stream)))

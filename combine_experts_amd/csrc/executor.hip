@@ -1,5 +1,5 @@
-// Layer executor: the five steps over micro-batches, optionally on two streams, with an optional
-// shared expert.
+// Layer executors: the forward's five steps over micro-batches, optionally on two streams, with an
+// optional shared expert; and the backward's steps in order.
 //
 // "Expert Parallelism and All-to-All" (DeepSeek-V3 splits the work into micro-batches so that the
 // exchange of one hides behind the computation of another) and the EP-in-LLMs article,
@@ -72,7 +72,8 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
     void* hc = static_cast<char*>(a->h) + p0 * (int64_t)d->F * eb;
     void* yp = static_cast<char*>(a->y_perm) + p0 * D * eb;
     int32_t* eoff = a->expert_offsets + ci * (E + 1);
-    if ((st = moe_route(&c, xc, a->w_gate, a->bias, a->topk_idx + p0, a->topk_gate + p0, nullptr, stream)) != MOE_OK)
+    float* lg = a->logits ? a->logits + ci * tc * E : nullptr;
+    if ((st = moe_route(&c, xc, a->w_gate, a->bias, a->topk_idx + p0, a->topk_gate + p0, lg, stream)) != MOE_OK)
       return st;
     if ((st = moe_dispatch_layout(&c, a->topk_idx + p0, a->expert_counts + ci * E, eoff, a->rank_counts + ci * ep,
                                   a->rank_offsets + ci * (ep + 1), a->pair_to_row + p0, a->row_to_pair + p0,
@@ -83,7 +84,12 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
       if (hipEventRecord(events[2 * ci], stream) != hipSuccess) return MOE_ERR_HIP;
       if (hipStreamWaitEvent(side_stream, events[2 * ci], 0) != hipSuccess) return MOE_ERR_HIP;
     }
-    if ((st = moe_expert_ffn_up(&c, xp, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) return st;
+    if (a->pre != nullptr) {
+      void* pc = static_cast<char*>(a->pre) + p0 * (int64_t)d->F * (d->act == MOE_ACT_SWIGLU ? 2 : 1) * eb;
+      if ((st = moe_expert_ffn_up_train(&c, xp, eoff, a->w1, a->w3, hc, pc, fs)) != MOE_OK) return st;
+    } else if ((st = moe_expert_ffn_up(&c, xp, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) {
+      return st;
+    }
     if ((st = moe_expert_ffn_down(&c, hc, eoff, a->w2, yp, fs)) != MOE_OK) return st;
     if (two && hipEventRecord(events[2 * ci + 1], side_stream) != hipSuccess) return MOE_ERR_HIP;
     if (a->shared_w1 != nullptr) {
@@ -100,6 +106,40 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
   }
   if (two && hipStreamWaitEvent(stream, events[2 * (n_chunks - 1) + 1], 0) != hipSuccess) return MOE_ERR_HIP;
   return combine(n_chunks - 1);
+}
+
+int moe_layer_backward(const moe_dims* d, const moe_backward_args* a, hipStream_t stream) {
+  if (d == nullptr || a == nullptr) return MOE_ERR_INVALID_ARG;
+  int st = MOE_OK;
+  const int nm = d->act == MOE_ACT_SWIGLU ? 2 : 1;
+  if (a->refresh_weights) {
+    if ((st = moe_transpose_weights(d, a->w1, a->w3, a->w2, a->w13t, a->w2t, stream)) != MOE_OK) return st;
+  }
+  if ((st = moe_backward_combine(d, a->dy, a->pair_to_row, a->topk_gate, a->y_perm, a->dy_perm, a->dgate, stream)) !=
+      MOE_OK)
+    return st;
+  if ((st = moe_expert_ffn_down_backward(d, a->dy_perm, a->expert_offsets, a->w2t, a->pre, a->da, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_expert_ffn_up_backward(d, a->da, a->expert_offsets, a->w13t, a->dx_perm, stream)) != MOE_OK) return st;
+  // a dropless forward layout doubles as the router's grouping of the pairs by expert
+  const bool grouped = d->capacity_factor <= 0.0;
+  if ((st = moe_router_backward(d, a->x, a->logits, a->topk_idx, a->topk_gate, a->dgate,
+                                grouped ? a->expert_offsets : nullptr, grouped ? a->row_to_pair : nullptr, a->dl,
+                                a->dw_gate, a->dbias, a->router_ws, a->router_ws_bytes, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_backward_dx(d, a->dx_perm, a->pair_to_row, a->topk_idx, a->dl, a->w_gate, a->dx, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_group_transpose(d, a->dy_perm, d->D, a->expert_offsets, a->koff, a->dy_perm_t, a->ld, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_group_transpose(d, a->h, d->F, a->expert_offsets, a->koff, a->h_t, a->ld, stream)) != MOE_OK) return st;
+  if ((st = moe_expert_wgrad(d, a->dy_perm_t, a->h_t, a->koff, d->D, d->F, a->ld, a->dw2, nullptr, d->D, stream)) !=
+      MOE_OK)
+    return st;
+  if ((st = moe_group_transpose(d, a->da, nm * d->F, a->expert_offsets, a->koff, a->da_t, a->ld, stream)) != MOE_OK)
+    return st;
+  if ((st = moe_group_transpose(d, a->x_perm, d->D, a->expert_offsets, a->koff, a->x_perm_t, a->ld, stream)) != MOE_OK)
+    return st;
+  return moe_expert_wgrad(d, a->da_t, a->x_perm_t, a->koff, nm * d->F, d->D, a->ld, a->dw1, a->dw3, d->F, stream);
 }
 
 }  // extern "C"

@@ -28,8 +28,8 @@ class MoELayerBuffers:
         self.rank_offsets = torch.empty(d.ep_size + 1, **i32)
         self.pair_to_row = torch.empty(P, **i32)
         self.row_to_pair = torch.empty(P, **i32)
-        self.layout_ws = torch.empty(max(1, L.moe_workspace_size(d, L.MOE_STAGE_LAYOUT)), dtype=torch.uint8,
-                                     device=device)
+        ws = (L.moe_workspace_size(d, L.MOE_STAGE_LAYOUT) + 255) // 256 * 256
+        self.layout_ws = torch.empty(max(256, ws), dtype=torch.uint8, device=device)
         self.x_perm = torch.empty((P, d.D), dtype=dt, device=device)
         self.h = torch.empty((P, d.F), dtype=dt, device=device)
         self.y_perm = torch.empty((P, d.D), dtype=dt, device=device)
@@ -39,16 +39,26 @@ class MoELayerBuffers:
         return {k: v for k, v in self.__dict__.items() if isinstance(v, torch.Tensor) or v is None}
 
 
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _layer_args(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, pre=None) -> L.moe_layer_args:
+    a = L.moe_layer_args()
+    a.x, a.w_gate, a.bias, a.w1, a.w3, a.w2, a.y = _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(w1), _ptr(w3), _ptr(w2), \
+        _ptr(buf.y)
+    for n in ("topk_idx", "topk_gate", "pair_to_row", "row_to_pair", "x_perm", "h", "y_perm", "expert_counts",
+              "expert_offsets", "rank_counts", "rank_offsets", "layout_ws", "logits"):
+        setattr(a, n, _ptr(getattr(buf, n)))
+    a.layout_ws_bytes = buf.layout_ws.numel()
+    a.pre = _ptr(pre)
+    return a
+
+
 def forward(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, stream=None) -> torch.Tensor:
-    """route -> dispatch layout -> permute -> expert FFN (up, down) -> unpermute + combine."""
-    d = buf.d
-    L.moe_route(d, x, w_gate, bias, buf.topk_idx, buf.topk_gate, buf.logits, stream)
-    L.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
-                          buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
-    L.moe_permute(d, x, buf.pair_to_row, buf.x_perm, stream)
-    L.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, w1, w3, buf.h, stream)
-    L.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, w2, buf.y_perm, stream)
-    L.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
+    """route -> dispatch layout -> permute -> expert FFN (up, down) -> unpermute + combine, as one call of
+    the library's executor (one micro-batch, one stream). Router logits land in buf.logits if it has them."""
+    L.moe_layer_forward(buf.d, _layer_args(buf, x, w_gate, bias, w1, w3, w2), 1, stream)
     return buf.y
 
 
@@ -149,39 +159,31 @@ class BackwardBuffers:
         self.dw2 = torch.empty((E, D, F), **f32)
 
 
-def forward_train(buf: MoELayerBuffers, bw: BackwardBuffers, x, w_gate, bias, w1, w3, w2, stream=None):
+def forward_train(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, bias, w1, w3, w2, stream=None):
     """The forward with what the backward needs saved: logits (buf must hold them) and pre-activations."""
-    d = buf.d
-    L.moe_route(d, x, w_gate, bias, buf.topk_idx, buf.topk_gate, buf.logits, stream)
-    L.moe_dispatch_layout(d, buf.topk_idx, buf.expert_counts, buf.expert_offsets, buf.rank_counts,
-                          buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
-    L.moe_permute(d, x, buf.pair_to_row, buf.x_perm, stream)
-    L.moe_expert_ffn_up_train(d, buf.x_perm, buf.expert_offsets, w1, w3, buf.h, bw.pre, stream)
-    L.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, w2, buf.y_perm, stream)
-    L.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
+    if buf.logits is None:
+        raise ValueError("forward_train needs MoELayerBuffers(..., logits=True)")
+    L.moe_layer_forward(buf.d, _layer_args(buf, x, w_gate, bias, w1, w3, w2, pre=bw.pre), 1, stream)
     return buf.y
 
 
-def backward(buf: MoELayerBuffers, bw: BackwardBuffers, x, w_gate, dy, stream=None, transpose_weights=None):
-    """The backward steps in order (``transpose_weights``: (w1, w3, w2) to refresh bw.w13t / bw.w2t first,
-    as after a weight update). Gradients land in bw.dx, bw.dw_gate, bw.dbias, bw.dw1, bw.dw3, bw.dw2."""
-    d = buf.d
-    nm = 2 if d.act == L.MOE_ACT_SWIGLU else 1
+def backward(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, dy, stream=None, transpose_weights=None):
+    """The backward as one call of the library's executor (``transpose_weights``: (w1, w3, w2) to rebuild
+    bw.w13t / bw.w2t first, as after a weight update). Gradients land in bw.dx, bw.dw_gate, bw.dbias,
+    bw.dw1, bw.dw3, bw.dw2."""
+    a = L.moe_backward_args()
+    a.x, a.w_gate, a.dy = _ptr(x), _ptr(w_gate), _ptr(dy)
     if transpose_weights is not None:
-        L.moe_transpose_weights(d, *transpose_weights, bw.w13t, bw.w2t, stream)
-    L.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm, bw.dy_perm, bw.dgate, stream)
-    L.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre, bw.da, stream)
-    L.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)
-    grouped = {}
-    if d.capacity_factor <= 0:  # the forward's layout is dropless: dW_g grouped by expert
-        grouped = dict(all_expert_offsets=buf.expert_offsets, all_row_to_pair=buf.row_to_pair)
-    L.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate, bw.dl, bw.dw_gate, bw.dbias,
-                          bw.router_ws, stream, **grouped)
-    L.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, w_gate, bw.dx, stream)
-    L.moe_group_transpose(d, bw.dy_perm, d.D, buf.expert_offsets, bw.koff, bw.dyp_t, stream)
-    L.moe_group_transpose(d, buf.h, d.F, buf.expert_offsets, bw.koff, bw.h_t, stream)
-    L.moe_expert_wgrad(d, bw.dyp_t, bw.h_t, bw.koff, d.D, d.F, bw.dw2, stream=stream)
-    L.moe_group_transpose(d, bw.da, nm * d.F, buf.expert_offsets, bw.koff, bw.da_t, stream)
-    L.moe_group_transpose(d, buf.x_perm, d.D, buf.expert_offsets, bw.koff, bw.xp_t, stream)
-    L.moe_expert_wgrad(d, bw.da_t, bw.xp_t, bw.koff, nm * d.F, d.D, bw.dw1, bw.dw3, split=d.F, stream=stream)
+        a.w1, a.w3, a.w2 = (_ptr(t) for t in transpose_weights)
+        a.refresh_weights = 1
+    for n in ("logits", "topk_idx", "topk_gate", "expert_offsets", "pair_to_row", "row_to_pair", "x_perm", "h",
+              "y_perm"):
+        setattr(a, n, _ptr(getattr(buf, n)))
+    for n in ("pre", "w13t", "w2t", "dy_perm", "dgate", "da", "dx_perm", "dl", "router_ws", "koff", "dx", "dw_gate",
+              "dbias", "dw1", "dw3", "dw2"):
+        setattr(a, n, _ptr(getattr(bw, n)))
+    a.router_ws_bytes = bw.router_ws.numel()
+    a.dy_perm_t, a.h_t, a.da_t, a.x_perm_t = _ptr(bw.dyp_t), _ptr(bw.h_t), _ptr(bw.da_t), _ptr(bw.xp_t)
+    a.ld = bw.dyp_t.shape[1]
+    L.moe_layer_backward(buf.d, a, stream)
     return bw.dx

@@ -303,6 +303,11 @@ typedef struct moe_layer_args {
   void* shared_h;            /* [T, shared_F] scratch */
   void* shared_y;            /* [T, D] scratch */
   const int32_t* shared_offsets; /* int32 [2] = {0, T/n_chunks} */
+  /* optional training outputs: the router's float32 logits [T, E] and the up-projection's
+   * pre-activations [T*top_k, 2F] (SwiGLU) or [T*top_k, F] (GELU), as moe_layer_backward reads them
+   * (pre: bf16 only) */
+  float* logits;
+  void* pre;
 } moe_layer_args;
 
 /* Runs the layer as above. side_stream NULL: everything on `stream`, micro-batch after micro-batch.
@@ -384,6 +389,25 @@ int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, cons
  * M = D, N = F); [dW1; dW3] = wgrad(da^T, x_perm^T, M = 2F (or F), N = D, split = F). */
 int moe_expert_wgrad(const moe_dims* d, const void* a_t, const void* b_t, const int32_t* koff, int32_t M,
                      int32_t N, int64_t ld, float* out0, float* out1, int32_t split, hipStream_t stream);
+
+/* The whole backward in order (the steps above), from one argument block. Buffers as the step entry
+ * points take them; `ld` = the row length of the transposed wgrad operands (>= moe_wgrad_ld()).
+ * refresh_weights != 0: rebuild w13t / w2t from w1, w3, w2 first (after a weight update). For a
+ * layer with a capacity factor, dW_g takes the dense form (the forward's layout is not dropless). */
+typedef struct moe_backward_args {
+  const void* x; const void* w_gate; const void* w1; const void* w3; const void* w2;
+  const float* logits; const int32_t* topk_idx; const float* topk_gate;
+  const int32_t* expert_offsets; const int32_t* pair_to_row; const int32_t* row_to_pair;
+  const void* x_perm; const void* h; const void* pre; const void* y_perm;   /* saved forward tensors */
+  const void* dy;                                                          /* [T, D] upstream gradient */
+  void* w13t; void* w2t; int32_t refresh_weights;
+  void* dy_perm; float* dgate; void* da; void* dx_perm; float* dl;         /* backward activations */
+  void* router_ws; size_t router_ws_bytes;
+  int32_t* koff; void* dy_perm_t; void* h_t; void* da_t; void* x_perm_t; int64_t ld;
+  void* dx; float* dw_gate; float* dbias; float* dw1; float* dw3; float* dw2;  /* gradients out */
+} moe_backward_args;
+
+int moe_layer_backward(const moe_dims* d, const moe_backward_args* a, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_str(int status);

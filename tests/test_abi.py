@@ -187,8 +187,8 @@ def test_cluster_and_padded_host_checks():
 
 
 def test_layer_args_struct_layout():
-    # 19 pointers, a size_t, 3 pointers, an int32 (padded to 8), 3 pointers
-    assert ctypes.sizeof(M.moe_layer_args) == 19 * 8 + 8 + 3 * 8 + 8 + 3 * 8
+    # 19 pointers, a size_t, 3 pointers, an int32 (padded to 8), 5 pointers
+    assert ctypes.sizeof(M.moe_layer_args) == 19 * 8 + 8 + 3 * 8 + 8 + 5 * 8
     assert M.moe_layer_args.layout_ws_bytes.offset == 19 * 8
     assert M.moe_layer_args.shared_F.offset == 19 * 8 + 8 + 3 * 8
 
@@ -231,3 +231,11 @@ def test_backward_host_checks():
     assert lib.moe_router_backward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None, fake, fake, None, None, 0,
                                    None) == M.MOE_ERR_INVALID_ARG
     assert M.moe_workspace_size(d, M.MOE_STAGE_ROUTER_BWD) == 1 * 8 * 4
+
+
+def test_backward_args_struct_layout():
+    # 18 pointers, int32 (padded), 6 pointers, size_t, pointer, 4 pointers, int64, 6 pointers
+    assert M.moe_backward_args.refresh_weights.offset == 18 * 8
+    assert M.moe_backward_args.router_ws_bytes.offset == 18 * 8 + 8 + 6 * 8
+    assert M.moe_backward_args.ld.offset == 18 * 8 + 8 + 6 * 8 + 8 + 8 + 4 * 8
+    assert ctypes.sizeof(M.moe_backward_args) == 18 * 8 + 8 + 6 * 8 + 8 + 8 + 4 * 8 + 8 + 6 * 8

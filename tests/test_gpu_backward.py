@@ -249,3 +249,42 @@ def test_backward_stages(name):
         err = P.rel_err_rows(P.f64(dx)[same], bwd["dx"][same])
         assert err.max() <= 5e-2, f"dx end to end: max rel err {err.max():.3e}"
         print(f"[backward] {name}: dx end-to-end max rel err {err.max():.2e} on {same.sum()} tokens", flush=True)
+
+
+@needs_gpu
+@pytest.mark.parametrize("name", ["dsv3_small", "gelu_k1_bias", "capacity"])
+def test_native_backward_equals_the_steps(name):
+    """moe_layer_backward (one call) gives the same bits as the step entry points called in order."""
+    cfg = CASES[name]
+    inp = W.make_inputs(cfg, "cuda")
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device="cuda", logits=True)
+    bw = M.BackwardBuffers(d, device="cuda")
+    M.forward_train(buf, bw, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    dy = torch.randn((cfg.T, cfg.D), generator=g, device="cuda").to(torch.bfloat16)
+    M.backward(buf, bw, inp["x"], inp["w_gate"], dy, transpose_weights=(inp["w1"], inp["w3"], inp["w2"]))
+    torch.cuda.synchronize()
+    native = {n: getattr(bw, n).clone() for n in ("dx", "dw_gate", "dbias", "dw1", "dw2", "dl", "dgate")}
+    if bw.dw3 is not None:
+        native["dw3"] = bw.dw3.clone()
+    # the same steps, one entry point at a time
+    nm = 2 if cfg.act == W.ACT_SWIGLU else 1
+    M.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm, bw.dy_perm, bw.dgate)
+    M.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre, bw.da)
+    M.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm)
+    grouped = dict(all_expert_offsets=buf.expert_offsets, all_row_to_pair=buf.row_to_pair) \
+        if cfg.capacity_factor <= 0 else {}
+    M.moe_router_backward(d, inp["x"], buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate, bw.dl, bw.dw_gate, bw.dbias,
+                          bw.router_ws, **grouped)
+    M.moe_backward_dx(d, bw.dx_perm, buf.pair_to_row, buf.topk_idx, bw.dl, inp["w_gate"], bw.dx)
+    M.moe_group_transpose(d, bw.dy_perm, cfg.D, buf.expert_offsets, bw.koff, bw.dyp_t)
+    M.moe_group_transpose(d, buf.h, cfg.F, buf.expert_offsets, bw.koff, bw.h_t)
+    M.moe_expert_wgrad(d, bw.dyp_t, bw.h_t, bw.koff, cfg.D, cfg.F, bw.dw2)
+    M.moe_group_transpose(d, bw.da, nm * cfg.F, buf.expert_offsets, bw.koff, bw.da_t)
+    M.moe_group_transpose(d, buf.x_perm, cfg.D, buf.expert_offsets, bw.koff, bw.xp_t)
+    M.moe_expert_wgrad(d, bw.da_t, bw.xp_t, bw.koff, nm * cfg.F, cfg.D, bw.dw1, bw.dw3, split=cfg.F)
+    torch.cuda.synchronize()
+    for n, v in native.items():
+        assert torch.equal(getattr(bw, n), v), f"{n}: native executor differs from the steps"
