@@ -483,7 +483,7 @@ def moe_router_backward(d: moe_dims, x, logits, topk_idx, topk_gate, dgate, dl, 
         _ptr(topk_gate, "topk_gate", f32, P, nullable=d.T == 0), _ptr(dgate, "dgate", f32, P, nullable=d.T == 0),
         _ptr(all_expert_offsets, "all_expert_offsets", i32, d.E + 1, nullable=True),
         _ptr(all_row_to_pair, "all_row_to_pair", i32, P, nullable=True),
-        _ptr(dl, "dl", f32, d.T * d.E), _ptr(dw_gate, "dw_gate", f32, d.E * d.D),
+        _ptr(dl, "dl", f32, d.T * d.E, nullable=d.T == 0), _ptr(dw_gate, "dw_gate", f32, d.E * d.D),
         _ptr(dbias, "dbias", f32, d.E, nullable=True), _ptr(ws, "ws", nullable=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check("moe_router_backward", st)
@@ -509,7 +509,8 @@ def moe_group_transpose(d: moe_dims, src, n_cols: int, expert_offsets, koff, dst
     dt = _elem_dtype(d)
     ld = dst.numel() // max(1, n_cols)
     st = load_library().moe_group_transpose(
-        ctypes.byref(d), _ptr(src, "src", dt), int(n_cols), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        ctypes.byref(d), _ptr(src, "src", dt, nullable=d.T == 0), int(n_cols),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
         _ptr(koff, "koff", torch.int32, d.E + 1), _ptr(dst, "dst", dt, n_cols * moe_wgrad_ld(d)), ld, _stream(stream))
     _check("moe_group_transpose", st)
 

@@ -276,7 +276,8 @@ int moe_padded_layout(const moe_dims* d, const int32_t* topk_idx, const int32_t*
   if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;  // the padded layout needs a capacity
   const int64_t C = capacity_of(d);
   if ((int64_t)d->E * C > INT32_MAX) return MOE_ERR_INVALID_ARG;
-  if (!padded_offsets || !slot_to_pair) return MOE_ERR_INVALID_ARG;
+  // with no slots (an empty batch) slot_to_pair is empty and may be NULL
+  if (!padded_offsets || (d->E * C > 0 && !slot_to_pair)) return MOE_ERR_INVALID_ARG;
   if (d->T > 0 && (!topk_idx || !expert_offsets || !pair_to_row || !row_to_pair || !pair_to_slot))
     return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_padded_layout(topk_idx, expert_offsets, pair_to_row, row_to_pair, d->T * d->top_k,
@@ -290,8 +291,8 @@ int moe_permute_padded(const moe_dims* d, const void* x, const int32_t* slot_to_
   if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;
   const int64_t n_slots = (int64_t)d->E * capacity_of(d);
   if (n_slots > INT32_MAX) return MOE_ERR_INVALID_ARG;
-  if (!slot_to_pair || !x_pad || (d->T > 0 && !x)) return MOE_ERR_INVALID_ARG;
-  if ((x && !aligned16(x)) || !aligned16(x_pad)) return MOE_ERR_INVALID_ARG;
+  if ((n_slots > 0 && (!slot_to_pair || !x_pad)) || (d->T > 0 && !x)) return MOE_ERR_INVALID_ARG;
+  if ((x && !aligned16(x)) || (x_pad && !aligned16(x_pad))) return MOE_ERR_INVALID_ARG;
   if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_permute_padded(x, slot_to_pair, n_slots, d->top_k, d->D * elem_bytes(d), x_pad,
                                                stream));
@@ -304,8 +305,10 @@ static int ffn_padded(const moe_dims* d, bool up, const void* a, const int32_t* 
   if (d->capacity_factor <= 0.0) return MOE_ERR_INVALID_ARG;
   const int64_t n_slots = (int64_t)d->E * capacity_of(d);
   if (n_slots > INT32_MAX) return MOE_ERR_INVALID_ARG;
-  if (!a || !padded_offsets || !b0 || !out || (up && d->act == MOE_ACT_SWIGLU && !b1)) return MOE_ERR_INVALID_ARG;
-  if (!aligned16(a) || !aligned16(b0) || !aligned16(out) || (b1 && !aligned16(b1))) return MOE_ERR_INVALID_ARG;
+  if (!padded_offsets || !b0 || (up && d->act == MOE_ACT_SWIGLU && !b1)) return MOE_ERR_INVALID_ARG;
+  if (n_slots > 0 && (!a || !out)) return MOE_ERR_INVALID_ARG;
+  if ((a && !aligned16(a)) || !aligned16(b0) || (out && !aligned16(out)) || (b1 && !aligned16(b1)))
+    return MOE_ERR_INVALID_ARG;
   if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
   moe::FfnArgs f = up ? moe::FfnArgs{a, padded_offsets, b0, d->act == MOE_ACT_SWIGLU ? b1 : nullptr, out,
                                      (int32_t)n_slots, d->E, d->D, d->F, d->act}
@@ -413,7 +416,8 @@ int moe_router_backward(const moe_dims* d, const void* x, const float* logits, c
                         size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
-  if (!dl || !dw_gate || (d->T > 0 && (!x || !logits || !topk_idx || !topk_gate || !dgate))) return MOE_ERR_INVALID_ARG;
+  // with no tokens dl is empty (it may be NULL); dW_g and dbias still come out as zeros
+  if (!dw_gate || (d->T > 0 && (!dl || !x || !logits || !topk_idx || !topk_gate || !dgate))) return MOE_ERR_INVALID_ARG;
   if ((all_expert_offsets == nullptr) != (all_row_to_pair == nullptr)) return MOE_ERR_INVALID_ARG;
   if (d->top_k > 32) return MOE_ERR_UNSUPPORTED;
   if (!row_vec_ok(d, d->D)) return MOE_ERR_UNSUPPORTED;
@@ -452,7 +456,7 @@ int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, cons
   int64_t need = 0;
   moe_wgrad_ld(d, &need);
   if (n_cols < 0 || ld < need) return MOE_ERR_INVALID_ARG;
-  if (!expert_offsets || !koff || (ld > 0 && n_cols > 0 && (!src || !dst))) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets || !koff || (ld > 0 && n_cols > 0 && (!dst || (d->T > 0 && !src)))) return MOE_ERR_INVALID_ARG;
   if (!row_vec_ok(d, n_cols)) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   hipError_t e = moe::launch_group_koff(expert_offsets, d->E, koff, stream);
   if (e == hipSuccess) e = moe::launch_group_transpose(src, n_cols, expert_offsets, koff, d->E, ld, dst, d->dtype, stream);

@@ -30,6 +30,10 @@
  *     row-indexed buffers are sized for the worst case N_max = T*top_k rows and kernels read
  *     N = expert_offsets[E] themselves. The host never waits on the GPU.
  *   - Pointers to element arrays must be 16-byte aligned.
+ *   - Empty inputs: T = 0 is valid everywhere. An array whose size is zero for the given dims (for
+ *     T = 0: x, the per-pair and per-row arrays, dy, dl; with no padded slots: slot_to_pair,
+ *     x_pad, h_pad, y_pad) may be NULL; outputs that do not scale with T (counts, offsets, weight
+ *     and bias gradients) are still written (zeros).
  *   - Errors: every entry point returns an int status (MOE_OK = 0). Argument checks run on the host
  *     before anything is enqueued; MOE_ERR_HIP reports a launch failure (hipGetLastError).
  *     Device-side preconditions (topk_idx values in [0,E)) are the caller's to keep.
