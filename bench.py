@@ -3,8 +3,11 @@
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3] [--no-cpu-baseline]
 
 One step = one full layer forward over one batch of seeded synthetic input already resident in
-HBM: all five stages, enqueued back to back on one stream with no host synchronisation. Prints
-ONE JSON line on stdout; diagnostics go to stderr.
+HBM: all five stages, enqueued back to back on one stream with no host synchronisation. The permute
+runs inside the up-projection's row loads (moe_expert_ffn_up_gather: the same h bit for bit as
+moe_permute + moe_expert_ffn_up); the standalone permute kernel, which the training forward uses, is
+timed on its own after the steps and reported as permute_gbps. Prints ONE JSON line on stdout;
+diagnostics go to stderr.
 
 value = T / (ms_per_step / 1e3) tokens/s on the one GPU. The roofline object is for the dominant
 kernel (the grouped up-projection GEMM with the fused SwiGLU/GELU epilogue), timed with HIP
@@ -27,7 +30,7 @@ METRIC = "MoE-layer tokens/s (route+permute+FFN+combine); permute GB/s; GEMM MFM
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-STAGES = ["route", "layout", "permute", "ffn_up", "ffn_down", "combine"]
+STAGES = ["route", "layout", "ffn_up", "ffn_down", "combine"]   # ffn_up includes the permute
 DOMINANT = "ffn_up"
 DOMINANT_SRC = os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip")
 CPU_SAMPLE_TOKENS = {"tiny_fp32": 256, "switch_cap": 2048, "mixtral": 64, "dsv3": 40, "skew": 256}
@@ -184,8 +187,8 @@ def measure_padded(M, W, torch, cfg, inp, stream, time_calls, cf=1.25):
 
 
 def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
-    """The layer executor: one stream vs n_chunks micro-batches on two streams, without and with a
-    shared expert of the routed experts' hidden size."""
+    """The layer executor (permute inside the up-projection, as in the step): one stream vs n_chunks
+    micro-batches on two streams, without and with a shared expert of the routed experts' hidden size."""
     d = M.dims_from_config(cfg)
     fs = cfg.F
     sh_cfg = cfg.replace(shared_F=fs)
@@ -195,7 +198,7 @@ def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
     for key, nc, two, use_sh in (("sequential_ms", 1, False, False), ("overlapped_ms", n_chunks, True, False),
                                  ("shared_sequential_ms", 1, False, True), ("shared_overlapped_ms", n_chunks, True, True),
                                  ("shared_concurrent_ms", 1, True, True)):
-        ex = M.LayerExecutor(d, n_chunks=nc, two_streams=two, shared_F=fs if use_sh else 0)
+        ex = M.LayerExecutor(d, n_chunks=nc, two_streams=two, shared_F=fs if use_sh else 0, gather=True)
         out[key] = round(time_calls(lambda: ex.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"],
                                                        inp["w2"], shared=shared if use_sh else None, stream=stream),
                                     reps=5), 4)
@@ -315,18 +318,16 @@ def main(argv=None):
                               buf.rank_offsets, buf.pair_to_row, buf.row_to_pair, buf.layout_ws, stream)
         if ev is not None:
             ev[2].record(stream)
-        M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+        M.moe_expert_ffn_up_gather(d, inp["x"], buf.row_to_pair, buf.expert_offsets, inp["w1"], inp["w3"], buf.h,
+                                   stream)
         if ev is not None:
             ev[3].record(stream)
-        M.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], buf.h, stream)
-        if ev is not None:
-            ev[4].record(stream)
         M.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm, stream)
         if ev is not None:
-            ev[5].record(stream)
+            ev[4].record(stream)
         M.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)
         if ev is not None:
-            ev[6].record(stream)
+            ev[5].record(stream)
 
     if args.copy_calib_bytes > 0:
         src = torch.ones(args.copy_calib_bytes, dtype=torch.uint8, device=dev)
@@ -338,7 +339,7 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -348,6 +349,15 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, s in enumerate(STAGES)}
+    # the standalone permute kernel (outside the timed steps), for its bandwidth
+    M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+    pa, pz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.record(stream)
+    for _ in range(20):
+        M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+    pz.record(stream)
+    torch.cuda.synchronize()
+    permute_ms = pa.elapsed_time(pz) / 20
 
     N = int(buf.expert_offsets[-1].item())
     counts = buf.expert_counts.cpu()
@@ -360,7 +370,7 @@ def main(argv=None):
     ffn_tflops = ffn_flops / ((stage_ms["ffn_up"] + stage_ms["ffn_down"]) * 1e-3) / 1e12
     permute_bytes = cfg.T * cfg.D * b + N * cfg.D * b + cfg.T * cfg.top_k * 4
     combine_bytes = N * cfg.D * b + cfg.T * cfg.D * b + cfg.T * cfg.top_k * 8
-    permute_gbs = permute_bytes / (stage_ms["permute"] * 1e-3) / 1e9
+    permute_gbs = permute_bytes / (permute_ms * 1e-3) / 1e9
     combine_gbs = combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9
     traffic = read_traffic(cfg.name)
     roofline = {"bound": "mfma", "achieved": round(up_tflops, 2), "peak": peak, "unit": "TFLOP/s",
@@ -443,7 +453,8 @@ def main(argv=None):
                    "ep_size_emulated": cfg.ep_size, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
                    "kept_rows": N, "parallelism": "1 GPU"},
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
-        "extra_stage_ms": {s: round(v, 4) for s, v in extra_ms.items()},
+        "permute": "inside ffn_up (rows gathered from x by the GEMM's loads)",
+        "extra_stage_ms": {"permute_standalone": round(permute_ms, 4), **{s: round(v, 4) for s, v in extra_ms.items()}},
         "cluster_emulation": cluster,
         "padded_capacity": padded,
         "overlap": overlap,

@@ -97,6 +97,7 @@ _SIG = {
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_up_gather": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_down": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
 }
@@ -254,6 +255,18 @@ def moe_expert_ffn_up(d: moe_dims, x_perm, expert_offsets, w1, w3, h, stream=Non
         _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
         _ptr(h, "h", dt, P * d.F), _stream(stream))
     _check("moe_expert_ffn_up", st)
+
+
+def moe_expert_ffn_up_gather(d: moe_dims, x, row_to_pair, expert_offsets, w1, w3, h, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up_gather(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D, nullable=d.T == 0),
+        _ptr(row_to_pair, "row_to_pair", torch.int32, P, nullable=d.T == 0),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(h, "h", dt, P * d.F, nullable=d.T == 0), _stream(stream))
+    _check("moe_expert_ffn_up_gather", st)
 
 
 def moe_expert_ffn_down(d: moe_dims, h, expert_offsets, w2, y_perm, stream=None) -> None:

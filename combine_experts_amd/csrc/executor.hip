@@ -10,7 +10,8 @@
 //   main:  R0 L0 P0 | S0 | R1 L1 P1 | S1 | wait F0, C0 | R2 L2 P2 | S2 | wait F1, C1 | ... | wait Fn-1, Cn-1
 //   side:            wait P0, F0 (up, down) | wait P1, F1 | ...
 //
-// R route, L layout, P permute, S shared expert, F grouped FFN, C combine (+ shared output). Every
+// R route, L layout, P permute, S shared expert, F grouped FFN, C combine (+ shared output). Without
+// an x_perm buffer there is no P: the up-projection of F gathers its rows from x itself. Every
 // micro-batch owns disjoint slices of the caller's buffers, so the two streams never write the same
 // memory; the main stream ends after the last combine, which waited for the last FFN, so all work
 // of the call is ordered before whatever the caller enqueues next on the main stream.
@@ -32,6 +33,7 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
   if (d == nullptr || a == nullptr) return MOE_ERR_INVALID_ARG;
   if (n_chunks < 1 || d->T % n_chunks != 0) return MOE_ERR_INVALID_ARG;
   if (side_stream != nullptr && events == nullptr) return MOE_ERR_INVALID_ARG;
+  if (a->x_perm == nullptr && a->pre != nullptr) return MOE_ERR_INVALID_ARG;  // training keeps x_perm
   if (a->shared_w1 != nullptr && (a->shared_F <= 0 || !a->shared_w2 || !a->shared_h || !a->shared_y ||
                                   !a->shared_offsets || (d->act == MOE_ACT_SWIGLU && !a->shared_w3)))
     return MOE_ERR_INVALID_ARG;
@@ -68,7 +70,7 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
   for (int64_t ci = 0; ci < n_chunks; ++ci) {
     const int64_t p0 = ci * tc * k;
     const void* xc = chunk(a->x, ci, tc * D * eb);
-    void* xp = static_cast<char*>(a->x_perm) + p0 * D * eb;
+    void* xp = a->x_perm ? static_cast<char*>(a->x_perm) + p0 * D * eb : nullptr;
     void* hc = static_cast<char*>(a->h) + p0 * (int64_t)d->F * eb;
     void* yp = static_cast<char*>(a->y_perm) + p0 * D * eb;
     int32_t* eoff = a->expert_offsets + ci * (E + 1);
@@ -79,7 +81,7 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
                                   a->rank_offsets + ci * (ep + 1), a->pair_to_row + p0, a->row_to_pair + p0,
                                   static_cast<char*>(a->layout_ws) + ci * ws_chunk, ws_chunk, stream)) != MOE_OK)
       return st;
-    if ((st = moe_permute(&c, xc, a->pair_to_row + p0, xp, stream)) != MOE_OK) return st;
+    if (xp && (st = moe_permute(&c, xc, a->pair_to_row + p0, xp, stream)) != MOE_OK) return st;
     if (two) {
       if (hipEventRecord(events[2 * ci], stream) != hipSuccess) return MOE_ERR_HIP;
       if (hipStreamWaitEvent(side_stream, events[2 * ci], 0) != hipSuccess) return MOE_ERR_HIP;
@@ -87,7 +89,9 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
     if (a->pre != nullptr) {
       void* pc = static_cast<char*>(a->pre) + p0 * (int64_t)d->F * (d->act == MOE_ACT_SWIGLU ? 2 : 1) * eb;
       if ((st = moe_expert_ffn_up_train(&c, xp, eoff, a->w1, a->w3, hc, pc, fs)) != MOE_OK) return st;
-    } else if ((st = moe_expert_ffn_up(&c, xp, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) {
+    } else if (xp) {
+      if ((st = moe_expert_ffn_up(&c, xp, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) return st;
+    } else if ((st = moe_expert_ffn_up_gather(&c, xc, a->row_to_pair + p0, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) {
       return st;
     }
     if ((st = moe_expert_ffn_down(&c, hc, eoff, a->w2, yp, fs)) != MOE_OK) return st;

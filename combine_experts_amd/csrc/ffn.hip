@@ -9,6 +9,8 @@
 // Two launches per FFN:
 //   up:   h[r, :]      = act(x_perm[r] · W1[e]^T, x_perm[r] · W3[e]^T)    (K = D, Nout = F)
 //   down: y_perm[r, :] = h[r] · W2[e]^T                                   (K = F, Nout = D)
+// The up-projection can also read its rows straight from x (x_perm[r] = x[row_to_pair[r] / k]):
+// the permutation then happens in the GEMM's own row loads and x_perm is never written.
 // Both operands are contiguous along K (weights are (out, in)), which is what the matrix cores
 // want: each lane feeds 8 consecutive K elements (16 bytes) per operand per instruction.
 //
@@ -278,7 +280,8 @@ template <int ACTFN, bool DUAL, int EPI = EPI_PLAIN>
 __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                      const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                      bf16_t* __restrict__ out, int E, int K, int Nout,
-                                                     bf16_t* __restrict__ pre) {
+                                                     bf16_t* __restrict__ pre, const int32_t* __restrict__ gather,
+                                                     int gdiv) {
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
   __shared__ bf16x8 lds[2 * G_STAGE];
   const int NT = (Nout + BNO - 1) / BNO;
@@ -301,7 +304,8 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     const int slot = i * GTH + wave * MOE_WAVE + lane;
     if (i * GTH < G_ACH) {
       const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
-      src[i] = Ab + (size_t)(row < mrows ? row : 0) * K + ch * 8;
+      const int r = row < mrows ? row : 0;
+      src[i] = (gather ? A + (size_t)(gather[row0 + r] / gdiv) * K : Ab + (size_t)r * K) + ch * 8;
     } else {
       const int bs = slot - G_ACH;
       const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
@@ -489,7 +493,8 @@ constexpr int FBM = 64, FBN = 64, FBK = 16;
 template <int ACT, bool DUAL>
 __global__ void __launch_bounds__(256) ffn_gemm_f32(const float* __restrict__ A, const int32_t* __restrict__ offsets,
                                                     const float* __restrict__ B0, const float* __restrict__ B1,
-                                                    float* __restrict__ out, int E, int K, int Nout) {
+                                                    float* __restrict__ out, int E, int K, int Nout,
+                                                    const int32_t* __restrict__ gather, int gdiv) {
   constexpr int NB = DUAL ? 2 : 1;
   __shared__ float As[FBK][FBM + 4];
   __shared__ float Bs[NB][FBK][FBN + 4];
@@ -501,12 +506,19 @@ __global__ void __launch_bounds__(256) ffn_gemm_f32(const float* __restrict__ A,
   Bb[0] = B0 + ((size_t)e * Nout + n0) * K;
   if constexpr (DUAL) Bb[NB - 1] = B1 + ((size_t)e * Nout + n0) * K;
   float acc[NB][4][4] = {};
+  // 64 rows x 16 k = 1024 values per stage: 4 per thread, the same 4 rows at every stage
+  const float* arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid + i * 256) / FBK;
+    const int r = row0 + (row < mrows ? row : 0);
+    arow[i] = A + (size_t)(gather ? gather[r] / gdiv : r) * K;
+  }
   for (int k0 = 0; k0 < K; k0 += FBK) {
-    // 64 rows x 16 k = 1024 values: 4 per thread
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int c = tid + i * 256, row = c / FBK, kk = c % FBK;
-      As[kk][row] = (row < mrows) ? A[(size_t)(row0 + row) * K + k0 + kk] : 0.f;
+      As[kk][row] = (row < mrows) ? arow[i][k0 + kk] : 0.f;
 #pragma unroll
       for (int m = 0; m < NB; ++m) Bs[m][kk][row] = (n0 + row < Nout) ? Bb[m][(size_t)row * K + k0 + kk] : 0.f;
     }
@@ -565,7 +577,7 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   bf16_t* pr = (bf16_t*)a.pre;
 #define MOE_FFN_LAUNCH(ACTV, DUALV, EPIV)                                                                          \
   hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, DUALV, EPIV>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, \
-                     a.K, a.Nout, pr)
+                     a.K, a.Nout, pr, a.gather, a.gather_div)
   if (a.epi == 1) {
     if (a.act == MOE_ACT_SWIGLU) MOE_FFN_LAUNCH(MOE_ACT_SWIGLU, true, EPI_PRE);
     else MOE_FFN_LAUNCH(MOE_ACT_GELU, false, EPI_PRE);
@@ -601,13 +613,13 @@ hipError_t launch_ffn_f32(const FfnArgs& a, hipStream_t s) {
   float* o = (float*)a.out;
   if (a.act == MOE_ACT_SWIGLU)
     hipLaunchKernelGGL((ffn_gemm_f32<MOE_ACT_SWIGLU, true>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o,
-                       a.E, a.K, a.Nout);
+                       a.E, a.K, a.Nout, a.gather, a.gather_div);
   else if (a.act == MOE_ACT_GELU)
     hipLaunchKernelGGL((ffn_gemm_f32<MOE_ACT_GELU, false>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o,
-                       a.E, a.K, a.Nout);
+                       a.E, a.K, a.Nout, a.gather, a.gather_div);
   else
     hipLaunchKernelGGL((ffn_gemm_f32<-1, false>), grid, dim3(256), 0, s, A, a.expert_offsets, b0, b1, o, a.E, a.K,
-                       a.Nout);
+                       a.Nout, a.gather, a.gather_div);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 104;
+constexpr int kAbiVersion = 105;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -177,6 +177,23 @@ int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const int32_t* expe
   if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
   moe::FfnArgs a{x_perm, expert_offsets, w1, d->act == MOE_ACT_SWIGLU ? w3 : nullptr, h,
                  d->T * d->top_k, d->E, d->D, d->F, d->act};
+  return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(a, stream) : moe::launch_ffn_f32(a, stream));
+}
+
+int moe_expert_ffn_up_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
+                             const int32_t* expert_offsets, const void* w1, const void* w3, void* h,
+                             hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !row_to_pair || !expert_offsets || !w1 || !h || (d->act == MOE_ACT_SWIGLU && !w3))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(h) || (w3 && !aligned16(w3))) return MOE_ERR_INVALID_ARG;
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  moe::FfnArgs a{x, expert_offsets, w1, d->act == MOE_ACT_SWIGLU ? w3 : nullptr, h,
+                 d->T * d->top_k, d->E, d->D, d->F, d->act};
+  a.gather = row_to_pair;
+  a.gather_div = d->top_k;
   return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(a, stream) : moe::launch_ffn_f32(a, stream));
 }
 

@@ -112,6 +112,10 @@ struct FfnArgs {
   int act;                    // up: MOE_ACT_*; down: -1 (no activation); epi 2: the activation to differentiate
   int epi = 0;                // 0 plain; 1 also store pre-activations to `pre`; 2 activation backward
   void* pre = nullptr;        // epi 1: written; epi 2: read ([N_max, 2F] SwiGLU, [N_max, F] GELU)
+  // when set, row r of A is row gather[r] / gather_div of `a` (up: a = x, gather = row_to_pair,
+  // gather_div = top_k), so the permuted copy of x is never materialised
+  const int32_t* gather = nullptr;
+  int32_t gather_div = 1;
 };
 hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff, int G, int M, int N, long long ld,
                              float* out0, float* out1, int split, hipStream_t s);

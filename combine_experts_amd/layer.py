@@ -14,7 +14,9 @@ from . import _lib as L
 
 
 class MoELayerBuffers:
-    def __init__(self, d: L.moe_dims, device="cuda", logits: bool = False):
+    def __init__(self, d: L.moe_dims, device="cuda", logits: bool = False, x_perm: bool = True):
+        """x_perm=False: no permuted copy of x; the forward's up-projection gathers its rows from x
+        (``moe_expert_ffn_up_gather``). Training (``forward_train``) needs x_perm."""
         self.d = d
         dt = torch.bfloat16 if d.dtype == L.MOE_BF16 else torch.float32
         P = d.T * d.top_k
@@ -30,7 +32,7 @@ class MoELayerBuffers:
         self.row_to_pair = torch.empty(P, **i32)
         ws = (L.moe_workspace_size(d, L.MOE_STAGE_LAYOUT) + 255) // 256 * 256
         self.layout_ws = torch.empty(max(256, ws), dtype=torch.uint8, device=device)
-        self.x_perm = torch.empty((P, d.D), dtype=dt, device=device)
+        self.x_perm = torch.empty((P, d.D), dtype=dt, device=device) if x_perm else None
         self.h = torch.empty((P, d.F), dtype=dt, device=device)
         self.y_perm = torch.empty((P, d.D), dtype=dt, device=device)
         self.y = torch.empty((d.T, d.D), dtype=dt, device=device)
@@ -57,7 +59,8 @@ def _layer_args(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, pre=None) -> 
 
 def forward(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, stream=None) -> torch.Tensor:
     """route -> dispatch layout -> permute -> expert FFN (up, down) -> unpermute + combine, as one call of
-    the library's executor (one micro-batch, one stream). Router logits land in buf.logits if it has them."""
+    the library's executor (one micro-batch, one stream); without buf.x_perm the permute happens inside
+    the up-projection's row loads. Router logits land in buf.logits if it has them."""
     L.moe_layer_forward(buf.d, _layer_args(buf, x, w_gate, bias, w1, w3, w2), 1, stream)
     return buf.y
 
@@ -67,7 +70,8 @@ class LayerExecutor:
     shared expert). Allocates once with torch; every call only enqueues the library's kernels."""
 
     def __init__(self, d: L.moe_dims, n_chunks: int = 1, two_streams: bool = False, shared_F: int = 0,
-                 device="cuda"):
+                 device="cuda", gather: bool = False):
+        """gather=True: no x_perm buffer; each micro-batch's up-projection reads its rows from x."""
         if d.T % n_chunks != 0:
             raise ValueError("T must split evenly into the micro-batches")
         self.d, self.n_chunks = d, n_chunks
@@ -78,7 +82,7 @@ class LayerExecutor:
         self.topk_gate = torch.empty(P, dtype=torch.float32, device=device)
         self.pair_to_row = torch.empty(P, **i32)
         self.row_to_pair = torch.empty(P, **i32)
-        self.x_perm = torch.empty((P, d.D), dtype=dt, device=device)
+        self.x_perm = None if gather else torch.empty((P, d.D), dtype=dt, device=device)
         self.h = torch.empty((P, d.F), dtype=dt, device=device)
         self.y_perm = torch.empty((P, d.D), dtype=dt, device=device)
         self.y = torch.empty((d.T, d.D), dtype=dt, device=device)
@@ -161,8 +165,8 @@ class BackwardBuffers:
 
 def forward_train(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, bias, w1, w3, w2, stream=None):
     """The forward with what the backward needs saved: logits (buf must hold them) and pre-activations."""
-    if buf.logits is None:
-        raise ValueError("forward_train needs MoELayerBuffers(..., logits=True)")
+    if buf.logits is None or buf.x_perm is None:
+        raise ValueError("forward_train needs MoELayerBuffers(..., logits=True, x_perm=True)")
     L.moe_layer_forward(buf.d, _layer_args(buf, x, w_gate, bias, w1, w3, w2, pre=bw.pre), 1, stream)
     return buf.y
 

@@ -186,6 +186,14 @@ int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_
 int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
                       const void* w1, const void* w3, void* h, hipStream_t stream);
 
+/* moe_permute followed by moe_expert_ffn_up in one launch: the up-projection reads row r straight from
+ * x[row_to_pair[r] / top_k] ([EPLLM] pipeline steps 2 and 4 with the permuted copy of x left out).
+ * Output identical bit for bit to the two calls. x [T,D] in; row_to_pair [T*top_k] int32 in (as
+ * moe_dispatch_layout wrote it: entries [0, N) are read); h [T*top_k, F] out. */
+int moe_expert_ffn_up_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
+                             const int32_t* expert_offsets, const void* w1, const void* w3, void* h,
+                             hipStream_t stream);
+
 /* Second half of moe_expert_ffn: y_perm[r] = W2[e] h[r]. h [T*top_k, F] in; y_perm [T*top_k, D] out. */
 int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_offsets,
                         const void* w2, void* y_perm, hipStream_t stream);
@@ -290,7 +298,8 @@ typedef struct moe_layer_args {
   float* topk_gate;          /* [T*top_k] */
   int32_t* pair_to_row;      /* [T*top_k] */
   int32_t* row_to_pair;      /* [T*top_k] */
-  void* x_perm;              /* [T*top_k, D] */
+  void* x_perm;              /* [T*top_k, D], or NULL: the up-projection gathers its rows from x
+                                (moe_expert_ffn_up_gather); required when pre is set */
   void* h;                   /* [T*top_k, F] */
   void* y_perm;              /* [T*top_k, D] */
   int32_t* expert_counts;    /* [n_chunks, E] */

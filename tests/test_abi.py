@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 104
+    assert M.moe_abi_version() == 105
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -92,6 +92,8 @@ def test_null_and_misaligned_pointers_rejected():
     assert lib.moe_permute(ctypes.byref(d), fake + 2, fake, fake, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_unpermute_combine(ctypes.byref(d), fake, fake, fake, fake + 8, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_expert_ffn_up(ctypes.byref(d), fake, fake, fake, None, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_up_gather(ctypes.byref(d), fake, None, fake, fake, fake, fake, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_ffn_up_gather(ctypes.byref(d), fake + 4, fake, fake, fake, fake, fake, None) == M.MOE_ERR_INVALID_ARG
 
 
 def test_unsupported_shapes_reported():

@@ -191,6 +191,14 @@ def test_full_size_sampled(name):
     # full-size permute property: every kept row equals its token's x row (checked on the GPU)
     r2p = buf.row_to_pair[:N].long()
     assert torch.equal(buf.x_perm[:N], inp["x"][r2p // cfg.top_k])
+    # the up-projection with the permute fused into its row loads (the form the benchmark times):
+    # the same h bit for bit
+    print("[parity-full] gather up-projection", flush=True)
+    h2 = torch.empty_like(buf.h)
+    M.moe_expert_ffn_up_gather(d, inp["x"], buf.row_to_pair, buf.expert_offsets, inp["w1"], inp["w3"], h2)
+    torch.cuda.synchronize()
+    assert torch.equal(h2[:N], buf.h[:N])
+    del h2
     print("[parity-full] ffn rows", len(rows), flush=True)
     wcache = {}
 
