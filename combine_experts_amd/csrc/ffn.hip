@@ -92,7 +92,9 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // accumulators 5 x 2 x 16 floats (255 VGPRs, no spills). 320 rows rather than 256: an expert with
 // 2*256 + a few rows, common when routing is near even, needs two tiles instead of three, and every
 // tile re-streams the expert's weights. The weight fragment is the MFMA's first operand, so each lane
-// ends up with 4 consecutive output columns of one token row: 8-byte stores in the epilogue.
+// ends up with 4 consecutive output columns of one token row; the plain epilogue regroups them in LDS
+// so that its global stores write 16-byte row pieces (the down-projection 6 % faster than storing
+// the 8-byte pieces directly).
 //
 // K runs in 64-deep stages through a 2-slot LDS ring (72 KB per slot). Loads go straight from
 // global memory into LDS (16 bytes per lane, no register staging); a whole stage is issued at once,
@@ -195,10 +197,29 @@ __device__ __forceinline__ int gbrow(int wn, int j) {
   else return wn * 64 + j * 32;
 }
 
+// LDS index (16-byte chunks) of a wave's fragment reads at k-step ks: A block i (rows (2i+wm)*32 + l)
+// at lane[ks] + a + i*64*GKCH, B block j (rows gbrow(wn,j) + l) at lane[ks] + b[j], l = lane % 32. The
+// blocks start at multiples of 32 rows, so the swizzle term depends on the lane alone.
+struct FragIdx {
+  int lane[G_KS];
+  int a, b[2];
+};
+
+template <bool DUAL>
+__device__ __forceinline__ FragIdx frag_idx(int lane, int wm, int wn) {
+  FragIdx f;
+  const int l = lane % 32;
+#pragma unroll
+  for (int ks = 0; ks < G_KS; ++ks) f.lane[ks] = l * GKCH + gswz(l, ks * 2 + lane / 32);
+  f.a = wm * 32 * GKCH;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) f.b[j] = G_ACH + gbrow<DUAL>(wn, j) * GKCH;
+  return f;
+}
+
 template <int ACT>  // active 32-row blocks of this wave
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
-                                           const int (&aoff)[G_KS][GMB], const int (&boff)[G_KS][2], int wave, int nk,
-                                           int mrows) {
+                                           const FragIdx& fi, int wave, int nk, int mrows) {
   // load i fills tile rows [i*64, i*64+64) of A (i < G_ACH/GTH) or a part of B; A loads wholly past
   // the tile's rows are skipped (those rows feed only accumulators that are never stored)
   auto issue = [&](int kt, int buf, int i) {
@@ -209,11 +230,11 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
   };
   bf16x8 fa[2][GMB], fb[2][2];
   auto frag = [&](int buf, int ks, int r) {
-    const bf16x8* s = lds + buf * G_STAGE;
+    const bf16x8* s = lds + buf * G_STAGE + fi.lane[ks];
 #pragma unroll
-    for (int i = 0; i < ACT; ++i) fa[r][i] = s[aoff[ks][i]];
+    for (int i = 0; i < ACT; ++i) fa[r][i] = s[fi.a + i * 2 * 32 * GKCH];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[r][j] = s[boff[ks][j]];
+    for (int j = 0; j < 2; ++j) fb[r][j] = s[fi.b[j]];
   };
 #pragma unroll
   for (int i = 0; i < G_LPS; ++i) issue(0, 0, i);
@@ -319,21 +340,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
       src[i] = p + ch * 8;
     }
   }
-  int aoff[G_KS][GMB], boff[G_KS][2];
-#pragma unroll
-  for (int ks = 0; ks < G_KS; ++ks) {
-    const int ch = ks * 2 + lane / 32;
-#pragma unroll
-    for (int i = 0; i < GMB; ++i) {
-      const int row = (2 * i + wm) * 32 + lane % 32;
-      aoff[ks][i] = row * GKCH + gswz(row, ch);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = gbrow<DUAL>(wn, j) + lane % 32;
-      boff[ks][j] = G_ACH + row * GKCH + gswz(row, ch);
-    }
-  }
+  const FragIdx fi = frag_idx<DUAL>(lane, wm, wn);
   const int nblk = (mrows + 31) / 32;
   const int act = __builtin_amdgcn_readfirstlane((nblk - wm + 1) / 2);  // blocks 2i+wm < nblk
   f32x16 acc[GMB][2];
@@ -346,14 +353,52 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
-    case 5: gemm_kloop<5>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
-    case 4: gemm_kloop<4>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
-    case 3: gemm_kloop<3>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
-    case 2: gemm_kloop<2>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
-    default: gemm_kloop<1>(acc, lds, src, aoff, boff, wave, nk, mrows); break;
+    case 5: gemm_kloop<5>(acc, lds, src, fi, wave, nk, mrows); break;
+    case 4: gemm_kloop<4>(acc, lds, src, fi, wave, nk, mrows); break;
+    case 3: gemm_kloop<3>(acc, lds, src, fi, wave, nk, mrows); break;
+    case 2: gemm_kloop<2>(acc, lds, src, fi, wave, nk, mrows); break;
+    default: gemm_kloop<1>(acc, lds, src, fi, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
   constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
+  if constexpr (EPI == EPI_PLAIN) {
+    // through LDS: each wave stages its 32-row blocks in the ring slot the last stage did not read
+    // (every wave passed the barrier after its last read of it) and stores whole 16-byte row pieces,
+    // WC/8 lanes per row, instead of 8-byte pieces of 32 rows per instruction
+    constexpr int WC = DUAL ? 32 : 64;  // output columns per wave
+    constexpr int SROW = WC + 8;        // staging row stride (elements; rows stay 16-byte aligned)
+    bf16_t* stg = reinterpret_cast<bf16_t*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROW;
+    const int cw = DUAL ? wn * 32 : wn * 64;
+#pragma unroll
+    for (int i = 0; i < GMB; ++i) {
+      if (i >= act) continue;
+      const int rl = lane % 32;
+#pragma unroll
+      for (int j = 0; j < (DUAL ? 1 : 2); ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int cl = j * 32 + 8 * q + 4 * (lane / 32);
+          bf16x4 pk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float h = acc[i][j][4 * q + u];
+            if constexpr (SWI && DUAL) h = act_silu_fast(h) * acc[i][1][4 * q + u];
+            else if constexpr (ACTFN == MOE_ACT_GELU) h = act_gelu(h);
+            pk[u] = f2bf(h);
+          }
+          *reinterpret_cast<bf16x4*>(stg + rl * SROW + cl) = pk;
+        }
+      constexpr int LPR = WC / 8, RPI = MOE_WAVE / LPR;
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int r2 = rr + lane / LPR, c2 = (lane % LPR) * 8;
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(stg + r2 * SROW + c2);
+        const int r = (2 * i + wm) * 32 + r2, c = cw + c2;
+        if (r < mrows && n0 + c < Nout) *reinterpret_cast<bf16x8*>(out + (size_t)(row0 + r) * Nout + n0 + c) = v;
+      }
+    }
+    return;
+  }
   const int ldo = (EPI == EPI_BWD && SWI) ? 2 * Nout : Nout;   // out row stride
   const int ldp = SWI ? 2 * Nout : Nout;                         // pre row stride
 #pragma unroll
@@ -445,21 +490,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
       src[i] = bT + (size_t)(n0 + row < N ? n0 + row : n0) * ld + k0 + ch * 8;
     }
   }
-  int aoff[G_KS][GMB], boff[G_KS][2];
-#pragma unroll
-  for (int ks = 0; ks < G_KS; ++ks) {
-    const int ch = ks * 2 + lane / 32;
-#pragma unroll
-    for (int i = 0; i < GMB; ++i) {
-      const int row = (2 * i + wm) * 32 + lane % 32;
-      aoff[ks][i] = row * GKCH + gswz(row, ch);
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = gbrow<false>(wn, j) + lane % 32;
-      boff[ks][j] = G_ACH + row * GKCH + gswz(row, ch);
-    }
-  }
+  const FragIdx fi = frag_idx<false>(lane, wm, wn);
   f32x16 acc[GMB][2];
 #pragma unroll
   for (int i = 0; i < GMB; ++i)
@@ -467,7 +498,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) gemm_kloop<GMB>(acc, lds, src, aoff, boff, wave, nk, mrows);  // uniform: an empty group writes zeros
+  if (nk > 0) gemm_kloop<GMB>(acc, lds, src, fi, wave, nk, mrows);  // uniform: an empty group writes zeros
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
     const int m = m0 + (2 * i + wm) * 32 + lane % 32;
