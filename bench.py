@@ -349,6 +349,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     stage_ms = {s: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, s in enumerate(STAGES)}
+    per_step = {s: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, s in enumerate(STAGES)}
+    stage_med = {s: v[len(v) // 2] for s, v in per_step.items()}
+    stage_min = {s: v[0] for s, v in per_step.items()}
     # the standalone permute kernel (outside the timed steps), for its bandwidth
     M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
     pa, pz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -373,7 +376,26 @@ def main(argv=None):
     permute_gbs = permute_bytes / (permute_ms * 1e-3) / 1e9
     combine_gbs = combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9
     traffic = read_traffic(cfg.name)
-    roofline = {"bound": "mfma", "achieved": round(up_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+    # every stage against its own roofline: algorithmic bytes and flops at the realised N, spec peaks
+    T_, D_, E_, k_, F_ = cfg.T, cfg.D, cfg.E, cfg.top_k, cfg.F
+    algo = {
+        "route": (T_ * D_ * b + E_ * D_ * b + T_ * k_ * 8, 2.0 * T_ * D_ * E_),
+        "layout": (3 * T_ * k_ * 4 + (2 * E_ + 2 * cfg.ep_size + 2) * 4, 0.0),
+        "ffn_up": (E_ * (nm - 1) * F_ * D_ * b + T_ * D_ * b + N * 4 + N * F_ * b, up_flops),
+        "ffn_down": (E_ * D_ * F_ * b + N * F_ * b + N * D_ * b, 2.0 * N * D_ * F_),
+        "combine": (combine_bytes, 2.0 * N * D_),
+    }
+    stage_roof = {}
+    for s_, (by, fl) in algo.items():
+        t_hbm = by / (PEAK_HBM_GBS * 1e9) * 1e3
+        t_cmp = fl / (peak * 1e12) * 1e3
+        bound = max(t_hbm, t_cmp)
+        stage_roof[s_] = {"bound": "hbm" if t_hbm >= t_cmp else ("mfma" if cfg.dtype == W.DT_BF16 else "alu"),
+                          "bound_ms": round(bound, 5), "frac": round(bound / stage_ms[s_], 4),
+                          "algorithmic_bytes": by, "algorithmic_flops": fl}
+    layer_bound = sum(v["bound_ms"] for v in stage_roof.values())
+    roofline = {"bound": "mfma" if cfg.dtype == W.DT_BF16 else "alu", "achieved": round(up_tflops, 2), "peak": peak,
+                "unit": "TFLOP/s",
                 "frac": round(up_tflops / peak, 4), "traffic": traffic,
                 "kernel": "ffn_gemm_bf16 (grouped up-projection, fused SwiGLU)" if cfg.dtype == W.DT_BF16
                 else "ffn_gemm_f32 (grouped up-projection)",
@@ -453,6 +475,11 @@ def main(argv=None):
                    "ep_size_emulated": cfg.ep_size, "n_groups": cfg.n_groups, "topk_groups": cfg.topk_groups,
                    "kept_rows": N, "parallelism": "1 GPU"},
         "stage_ms": {s: round(v, 4) for s, v in stage_ms.items()},
+        "stage_ms_median": {s: round(v, 4) for s, v in stage_med.items()},
+        "stage_ms_min": {s: round(v, 4) for s, v in stage_min.items()},
+        "stage_roofline": stage_roof,
+        "layer_roofline": {"bound_ms": round(layer_bound, 4), "frac": round(layer_bound / ms_per_step, 4),
+                           "note": "sum of the stages' spec-peak bounds over the measured step"},
         "permute": "inside ffn_up (rows gathered from x by the GEMM's loads)",
         "extra_stage_ms": {"permute_standalone": round(permute_ms, 4), **{s: round(v, 4) for s, v in extra_ms.items()}},
         "cluster_emulation": cluster,
