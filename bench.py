@@ -208,7 +208,8 @@ def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
 
 
 def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
-    """One training step's backward at the workload shape, stage by stage (HIP events on the stream)."""
+    """One training step's backward at the workload shape, stage by stage (HIP events on the stream); the
+    data-gradient GEMMs read the weights as stored (no transposed copies to rebuild after an update)."""
     d = M.dims_from_config(cfg)
     buf = M.MoELayerBuffers(d, device="cuda", logits=True)
     bw = M.BackwardBuffers(d, device="cuda")
@@ -218,12 +219,11 @@ def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
     nm = 2 if cfg.act == W.ACT_SWIGLU else 1
     x, w1, w3, w2 = inp["x"], inp["w1"], inp["w3"], inp["w2"]
     stages = [
-        ("transpose_weights", lambda: M.moe_transpose_weights(d, w1, w3, w2, bw.w13t, bw.w2t, stream)),
         ("backward_combine", lambda: M.moe_backward_combine(d, dy, buf.pair_to_row, buf.topk_gate, buf.y_perm,
                                                             bw.dy_perm, bw.dgate, stream)),
-        ("dgrad_down_act", lambda: M.moe_expert_ffn_down_backward(d, bw.dy_perm, buf.expert_offsets, bw.w2t, bw.pre,
-                                                                  bw.da, stream)),
-        ("dgrad_up", lambda: M.moe_expert_ffn_up_backward(d, bw.da, buf.expert_offsets, bw.w13t, bw.dx_perm, stream)),
+        ("dgrad_down_act", lambda: M.moe_expert_ffn_down_backward_w(d, bw.dy_perm, buf.expert_offsets, w2, bw.pre,
+                                                                    bw.da, stream)),
+        ("dgrad_up", lambda: M.moe_expert_ffn_up_backward_w(d, bw.da, buf.expert_offsets, w1, w3, bw.dx_perm, stream)),
         ("router_backward", lambda: M.moe_router_backward(d, x, buf.logits, buf.topk_idx, buf.topk_gate, bw.dgate,
                                                           bw.dl, bw.dw_gate, bw.dbias, bw.router_ws, stream,
                                                           all_expert_offsets=buf.expert_offsets,
@@ -261,7 +261,7 @@ def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
     N = int(buf.expert_offsets[-1].item())
     gemm_flops = 2.0 * N * cfg.D * cfg.F * (1 + nm + 1 + nm)
     gemm_ms = st["dgrad_down_act"] + st["dgrad_up"] + st["wgrad_w2"] + st["wgrad_w13"]
-    total = sum(v for k_, v in st.items() if k_ != "transpose_weights")
+    total = sum(st.values())
     out = {"stage_ms": {k_: round(v, 4) for k_, v in st.items()}, "total_ms": round(total, 4),
            "forward_train_ms": round(fwd_ms, 4), "train_step_ms": round(fwd_ms + total, 4),
            "gemm_tflops": round(gemm_flops / (gemm_ms * 1e-3) / 1e12, 1),
@@ -452,8 +452,7 @@ def main(argv=None):
             f"{overlap['shared_sequential_ms']:.3f} / {overlap['shared_overlapped_ms']:.3f} ms, shared expert beside the "
             f"routed FFN on one batch {overlap['shared_concurrent_ms']:.3f} ms")
         if bwd is not None:
-            log(f"[bench] backward {bwd['total_ms']:.3f} ms (+ weight transposes {bwd['stage_ms']['transpose_weights']:.3f} ms "
-                f"once per update); grouped GEMMs {bwd['gemm_tflops']:.0f} TFLOP/s; training step (forward with saved "
+            log(f"[bench] backward {bwd['total_ms']:.3f} ms (weights read as stored); grouped GEMMs {bwd['gemm_tflops']:.0f} TFLOP/s; training step (forward with saved "
                 f"pre-activations + backward) {bwd['train_step_ms']:.3f} ms")
             for s_, v in bwd["stage_ms"].items():
                 log(f"[bench]     bwd {s_:20s} {v * 1e3:9.1f} us")

@@ -82,6 +82,8 @@ _SIG = {
     "moe_backward_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_down_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_up_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_down_backward_w": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_up_backward_w": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_router_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
     "moe_backward_dx": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
@@ -483,6 +485,27 @@ def moe_expert_ffn_up_backward(d: moe_dims, da, expert_offsets, w13t, dx_perm, s
         _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1), _ptr(w13t, "w13t", dt, d.E * d.F * d.D * _nm(d)),
         _ptr(dx_perm, "dx_perm", dt, P * d.D), _stream(stream))
     _check("moe_expert_ffn_up_backward", st)
+
+
+def moe_expert_ffn_down_backward_w(d: moe_dims, dy_perm, expert_offsets, w2, pre, da, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_down_backward_w(
+        ctypes.byref(d), _ptr(dy_perm, "dy_perm", dt, P * d.D),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1), _ptr(w2, "w2", dt, d.E * d.D * d.F),
+        _ptr(pre, "pre", dt, P * d.F * _nm(d)), _ptr(da, "da", dt, P * d.F * _nm(d)), _stream(stream))
+    _check("moe_expert_ffn_down_backward_w", st)
+
+
+def moe_expert_ffn_up_backward_w(d: moe_dims, da, expert_offsets, w1, w3, dx_perm, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up_backward_w(
+        ctypes.byref(d), _ptr(da, "da", dt, P * d.F * _nm(d)),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1), _ptr(w1, "w1", dt, d.E * d.F * d.D),
+        _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU), _ptr(dx_perm, "dx_perm", dt, P * d.D),
+        _stream(stream))
+    _check("moe_expert_ffn_up_backward_w", st)
 
 
 def moe_router_backward(d: moe_dims, x, logits, topk_idx, topk_gate, dgate, dl, dw_gate, dbias=None, ws=None,

@@ -116,15 +116,20 @@ int moe_layer_backward(const moe_dims* d, const moe_backward_args* a, hipStream_
   if (d == nullptr || a == nullptr) return MOE_ERR_INVALID_ARG;
   int st = MOE_OK;
   const int nm = d->act == MOE_ACT_SWIGLU ? 2 : 1;
-  if (a->refresh_weights) {
+  // without transposed copies the data-gradient GEMMs read the weights as stored
+  const bool natural = a->w13t == nullptr && a->w2t == nullptr;
+  if (a->refresh_weights && !natural) {
     if ((st = moe_transpose_weights(d, a->w1, a->w3, a->w2, a->w13t, a->w2t, stream)) != MOE_OK) return st;
   }
   if ((st = moe_backward_combine(d, a->dy, a->pair_to_row, a->topk_gate, a->y_perm, a->dy_perm, a->dgate, stream)) !=
       MOE_OK)
     return st;
-  if ((st = moe_expert_ffn_down_backward(d, a->dy_perm, a->expert_offsets, a->w2t, a->pre, a->da, stream)) != MOE_OK)
-    return st;
-  if ((st = moe_expert_ffn_up_backward(d, a->da, a->expert_offsets, a->w13t, a->dx_perm, stream)) != MOE_OK) return st;
+  st = natural ? moe_expert_ffn_down_backward_w(d, a->dy_perm, a->expert_offsets, a->w2, a->pre, a->da, stream)
+               : moe_expert_ffn_down_backward(d, a->dy_perm, a->expert_offsets, a->w2t, a->pre, a->da, stream);
+  if (st != MOE_OK) return st;
+  st = natural ? moe_expert_ffn_up_backward_w(d, a->da, a->expert_offsets, a->w1, a->w3, a->dx_perm, stream)
+               : moe_expert_ffn_up_backward(d, a->da, a->expert_offsets, a->w13t, a->dx_perm, stream);
+  if (st != MOE_OK) return st;
   // a dropless forward layout doubles as the router's grouping of the pairs by expert
   const bool grouped = d->capacity_factor <= 0.0;
   if ((st = moe_router_backward(d, a->x, a->logits, a->topk_idx, a->topk_gate, a->dgate,

@@ -197,6 +197,34 @@ __device__ __forceinline__ int gbrow(int wn, int j) {
   else return wn * 64 + j * 32;
 }
 
+constexpr int G_NAL = G_ACH / GTH;  // A loads per stage and lane
+
+// B stored K-major per expert ([K][N], N contiguous: the weights as the forward keeps them, read by
+// the data-gradient GEMMs). A stage's B slice is 64 rows of 256 columns (512 bytes each) in LDS, the
+// 16-byte chunk c of row k stored at chunk c ^ 4*(k & 3). Rows k < ksplit come from b0 (per expert
+// [ksplit][nout]), the rest from b1 (per expert [K - ksplit][nout]).
+struct BtSrc {
+  const bf16_t* b0;
+  const bf16_t* b1;
+  int ksplit, nout;
+  int ofs[G_LPS - G_NAL];  // this lane's element offset (row * nout + column) inside a stage, per B load
+  int tro[2][2];           // byte offsets of the transposed fragment reads (k half h, block j) in the B region
+  __device__ __forceinline__ const bf16_t* stage(int kt) const {
+    const int k0 = kt * GBK;
+    return k0 < ksplit ? b0 + (size_t)k0 * nout : b1 + (size_t)(k0 - ksplit) * nout;
+  }
+};
+
+// ds_read_b64_tr_b16: within each 16-lane group, output lane i gets element e from the group's lane
+// 4e + i/4, its element i % 4 (measured on the hardware). With lane 4e + q of the group reading row
+// k0 + e, columns c0 + 4q .. + 3, lane i receives rows k0 .. k0 + 3 of column c0 + i.
+__device__ __forceinline__ bf16x4 tr_read(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 // LDS index (16-byte chunks) of a wave's fragment reads at k-step ks: A block i (rows (2i+wm)*32 + l)
 // at lane[ks] + a + i*64*GKCH, B block j (rows gbrow(wn,j) + l) at lane[ks] + b[j], l = lane % 32. The
 // blocks start at multiples of 32 rows, so the swizzle term depends on the lane alone.
@@ -217,14 +245,15 @@ __device__ __forceinline__ FragIdx frag_idx(int lane, int wm, int wn) {
   return f;
 }
 
-template <int ACT>  // active 32-row blocks of this wave
+template <int ACT, bool BT>  // ACT: active 32-row blocks of this wave; BT: B stored K-major
 __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
-                                           const FragIdx& fi, int wave, int nk, int mrows) {
-  // load i fills tile rows [i*64, i*64+64) of A (i < G_ACH/GTH) or a part of B; A loads wholly past
-  // the tile's rows are skipped (those rows feed only accumulators that are never stored)
+                                           const FragIdx& fi, const BtSrc& bt, int wave, int nk, int mrows) {
+  // load i fills tile rows [i*64, i*64+64) of A (i < G_NAL) or a part of B; A loads wholly past the
+  // tile's rows are skipped (those rows feed only accumulators that are never stored)
   auto issue = [&](int kt, int buf, int i) {
-    if (i * GTH < G_ACH && i * (GTH / GKCH) >= mrows) return;
-    __builtin_amdgcn_global_load_lds((const void*)(src[i] + kt * GBK),
+    if (i < G_NAL && i * (GTH / GKCH) >= mrows) return;
+    const bf16_t* p = (BT && i >= G_NAL) ? bt.stage(kt) + bt.ofs[i - G_NAL] : src[i] + kt * GBK;
+    __builtin_amdgcn_global_load_lds((const void*)p,
                                      (__attribute__((address_space(3))) void*)(lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE),
                                      16, 0, 0);
   };
@@ -233,8 +262,18 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
     const bf16x8* s = lds + buf * G_STAGE + fi.lane[ks];
 #pragma unroll
     for (int i = 0; i < ACT; ++i) fa[r][i] = s[fi.a + i * 2 * 32 * GKCH];
+    if constexpr (BT) {
+      // two transposed 8-byte reads per fragment: 4 consecutive k of this lane's column each
+      const char* sb = reinterpret_cast<const char*>(lds + buf * G_STAGE + G_ACH) + ks * 16 * GBR * 2;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) fb[r][j] = s[fi.b[j]];
+      for (int j = 0; j < 2; ++j) {
+        const bf16x4 lo = tr_read(sb + bt.tro[0][j]), hi = tr_read(sb + bt.tro[1][j]);
+        fb[r][j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[r][j] = s[fi.b[j]];
+    }
   };
 #pragma unroll
   for (int i = 0; i < G_LPS; ++i) issue(0, 0, i);
@@ -268,7 +307,7 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
       // issue order: each fragment read for the next k-step goes right after one MFMA of this one,
       // rather than all reads in a batch behind a wait (measured 2-4 % faster, same results)
       {
-        constexpr int NR = 2 + ACT, NM = 2 * ACT, NP = NR < NM ? NR : NM;
+        constexpr int NR = (BT ? 4 : 2) + ACT, NM = 2 * ACT, NP = NR < NM ? NR : NM;
 #pragma unroll
         for (int q = 0; q < NP; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -297,12 +336,13 @@ __device__ __forceinline__ float act_gelu_grad(float a) {
 //              GELU out[r, n] = dh*GELU'(a1) (Nout wide)
 constexpr int EPI_PLAIN = 0, EPI_PRE = 1, EPI_BWD = 2;
 
-template <int ACTFN, bool DUAL, int EPI = EPI_PLAIN>
+template <int ACTFN, bool DUAL, int EPI = EPI_PLAIN, bool BT = false>
 __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                      const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                      bf16_t* __restrict__ out, int E, int K, int Nout,
                                                      bf16_t* __restrict__ pre, const int32_t* __restrict__ gather,
-                                                     int gdiv) {
+                                                     int gdiv, int ksplit) {
+  static_assert(!(BT && DUAL), "the K-major B form has no paired W1/W3 tile");
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
   __shared__ bf16x8 lds[2 * G_STAGE];
   const int NT = (Nout + BNO - 1) / BNO;
@@ -327,7 +367,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
       const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
       const int r = row < mrows ? row : 0;
       src[i] = (gather ? A + (size_t)(gather[row0 + r] / gdiv) * K : Ab + (size_t)r * K) + ch * 8;
-    } else {
+    } else if constexpr (!BT) {
       const int bs = slot - G_ACH;
       const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
       const bf16_t* p;
@@ -338,9 +378,33 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
         p = (n0 + row < Nout) ? Bw0 + (size_t)row * K : Bw0;
       }
       src[i] = p + ch * 8;
+    } else {
+      src[i] = nullptr;  // the K-major B loads go through bt
     }
   }
   const FragIdx fi = frag_idx<DUAL>(lane, wm, wn);
+  BtSrc bt{};
+  if constexpr (BT) {
+    bt.b0 = B0 + (size_t)e * ksplit * Nout + n0;
+    bt.b1 = B1 ? B1 + (size_t)e * (K - ksplit) * Nout + n0 : nullptr;
+    bt.ksplit = ksplit;
+    bt.nout = Nout;
+#pragma unroll
+    for (int i = G_NAL; i < G_LPS; ++i) {
+      const int bs = i * GTH + wave * MOE_WAVE + lane - G_ACH;  // chunk of the B region this lane fills
+      const int k = bs / (GBR / 8), c = (bs % (GBR / 8)) ^ ((k & 3) << 2);
+      bt.ofs[i - G_NAL] = k * Nout + (n0 + c * 8 < Nout ? c * 8 : 0);  // columns past Nout: never stored
+    }
+    const int g = lane / 16, e4 = (lane % 16) / 4, q = lane % 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = (g / 2) * 8 + 4 * h + e4;  // row & 3 == e4
+        const int c = (gbrow<false>(wn, j) / 8 + (g % 2) * 2 + q / 2) ^ (e4 << 2);
+        bt.tro[h][j] = row * GBR * 2 + c * 16 + (q % 2) * 8;
+      }
+  }
   const int nblk = (mrows + 31) / 32;
   const int act = __builtin_amdgcn_readfirstlane((nblk - wm + 1) / 2);  // blocks 2i+wm < nblk
   f32x16 acc[GMB][2];
@@ -353,11 +417,11 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
-    case 5: gemm_kloop<5>(acc, lds, src, fi, wave, nk, mrows); break;
-    case 4: gemm_kloop<4>(acc, lds, src, fi, wave, nk, mrows); break;
-    case 3: gemm_kloop<3>(acc, lds, src, fi, wave, nk, mrows); break;
-    case 2: gemm_kloop<2>(acc, lds, src, fi, wave, nk, mrows); break;
-    default: gemm_kloop<1>(acc, lds, src, fi, wave, nk, mrows); break;
+    case 5: gemm_kloop<5, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
+    case 4: gemm_kloop<4, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
+    case 3: gemm_kloop<3, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
+    case 2: gemm_kloop<2, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
+    default: gemm_kloop<1, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
   constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
@@ -498,7 +562,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) gemm_kloop<GMB>(acc, lds, src, fi, wave, nk, mrows);  // uniform: an empty group writes zeros
+  if (nk > 0) gemm_kloop<GMB, false>(acc, lds, src, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
     const int m = m0 + (2 * i + wm) * 32 + lane % 32;
@@ -597,7 +661,7 @@ dim3 ffn_grid(const FfnArgs& a, int tbn) {
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   if (a.n_rows_max == 0) return hipSuccess;
   // the up-projection tile pairs W1 and W3 rows (SwiGLU forward); every other form is a plain tile
-  const bool dual = a.act == MOE_ACT_SWIGLU && a.epi != 2;
+  const bool dual = a.act == MOE_ACT_SWIGLU && a.epi != 2 && !a.bt;
   const int bno = dual ? GBR / 2 : GBR;
   const long long row_tiles = (a.n_rows_max + GBM - 1) / GBM + (a.E < a.n_rows_max ? a.E : a.n_rows_max);
   const dim3 grid((unsigned)(row_tiles * ((a.Nout + bno - 1) / bno) + 8));
@@ -608,8 +672,18 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   bf16_t* pr = (bf16_t*)a.pre;
 #define MOE_FFN_LAUNCH(ACTV, DUALV, EPIV)                                                                          \
   hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, DUALV, EPIV>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, \
-                     a.K, a.Nout, pr, a.gather, a.gather_div)
-  if (a.epi == 1) {
+                     a.K, a.Nout, pr, a.gather, a.gather_div, 0)
+#define MOE_FFN_LAUNCH_BT(ACTV, EPIV)                                                                              \
+  hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, false, EPIV, true>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, \
+                     a.E, a.K, a.Nout, pr, a.gather, a.gather_div, a.ksplit > 0 ? a.ksplit : a.K)
+  if (a.bt) {
+    if (a.K % GBK != 0 || (a.ksplit > 0 && (a.ksplit % GBK != 0 || a.ksplit > a.K || (a.ksplit < a.K && !b1))))
+      return hipErrorInvalidValue;
+    if (a.epi == 2 && a.act == MOE_ACT_SWIGLU) MOE_FFN_LAUNCH_BT(MOE_ACT_SWIGLU, EPI_BWD);
+    else if (a.epi == 2) MOE_FFN_LAUNCH_BT(MOE_ACT_GELU, EPI_BWD);
+    else if (a.epi == 0 && a.act < 0) MOE_FFN_LAUNCH_BT(-1, EPI_PLAIN);
+    else return hipErrorInvalidValue;
+  } else if (a.epi == 1) {
     if (a.act == MOE_ACT_SWIGLU) MOE_FFN_LAUNCH(MOE_ACT_SWIGLU, true, EPI_PRE);
     else MOE_FFN_LAUNCH(MOE_ACT_GELU, false, EPI_PRE);
   } else if (a.epi == 2) {
@@ -623,6 +697,7 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
     MOE_FFN_LAUNCH(-1, false, EPI_PLAIN);
   }
 #undef MOE_FFN_LAUNCH
+#undef MOE_FFN_LAUNCH_BT
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 105;
+constexpr int kAbiVersion = 106;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -424,6 +424,36 @@ int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t*
   if (!aligned16(da) || !aligned16(w13t) || !aligned16(dx_perm)) return MOE_ERR_INVALID_ARG;
   const int K = (d->act == MOE_ACT_SWIGLU ? 2 : 1) * d->F;
   moe::FfnArgs a{da, expert_offsets, w13t, nullptr, dx_perm, d->T * d->top_k, d->E, K, d->D, -1};
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
+int moe_expert_ffn_down_backward_w(const moe_dims* d, const void* dy_perm, const int32_t* expert_offsets,
+                                   const void* w2, const void* pre, void* da, hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!dy_perm || !expert_offsets || !w2 || !pre || !da) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(dy_perm) || !aligned16(w2) || !aligned16(pre) || !aligned16(da)) return MOE_ERR_INVALID_ARG;
+  // dh = dy_perm W2 with W2[e] read as stored, [D][F]: K = D rows of F columns
+  moe::FfnArgs a{dy_perm, expert_offsets, w2, nullptr, da, d->T * d->top_k, d->E, d->D, d->F, d->act, 2,
+                 const_cast<void*>(pre)};
+  a.bt = 1;
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
+int moe_expert_ffn_up_backward_w(const moe_dims* d, const void* da, const int32_t* expert_offsets, const void* w1,
+                                 const void* w3, void* dx_perm, hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  const bool swi = d->act == MOE_ACT_SWIGLU;
+  if (!da || !expert_offsets || !w1 || !dx_perm || (swi && !w3)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(da) || !aligned16(w1) || !aligned16(dx_perm) || (swi && !aligned16(w3))) return MOE_ERR_INVALID_ARG;
+  // dx_perm = [da1 | da3] [W1; W3]: W1[e], W3[e] read as stored, [F][D]; reduction rows k < F from W1
+  moe::FfnArgs a{da, expert_offsets, w1, swi ? w3 : nullptr, dx_perm, d->T * d->top_k, d->E,
+                 (swi ? 2 : 1) * d->F, d->D, -1};
+  a.bt = 1;
+  a.ksplit = d->F;
   return hip_status(moe::launch_ffn_bf16(a, stream));
 }
 

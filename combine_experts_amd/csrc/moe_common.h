@@ -116,6 +116,11 @@ struct FfnArgs {
   // gather_div = top_k), so the permuted copy of x is never materialised
   const int32_t* gather = nullptr;
   int32_t gather_div = 1;
+  // bf16 data-gradient forms only: b0 (and b1) stored K-major per expert, [K][Nout] (the weights as the
+  // forward keeps them); with b1, rows k < ksplit of the reduction come from b0 ([ksplit][Nout] per
+  // expert) and the rest from b1 ([K - ksplit][Nout])
+  int bt = 0;
+  int32_t ksplit = 0;
 };
 hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff, int G, int M, int N, long long ld,
                              float* out0, float* out1, int split, hipStream_t s);

@@ -130,18 +130,20 @@ class LayerExecutor:
 
 
 class BackwardBuffers:
-    """Buffers of one training step's backward for dims d (bf16): saved pre-activations, transposed
-    weights, the backward's activations, transposed wgrad operands and float32 gradients."""
+    """Buffers of one training step's backward for dims d (bf16): saved pre-activations, the backward's
+    activations, transposed wgrad operands and float32 gradients. transposed=True also keeps transposed
+    copies of the weights (w13t, w2t) for the data-gradient GEMMs; by default they read the weights as
+    stored."""
 
-    def __init__(self, d: L.moe_dims, device="cuda"):
+    def __init__(self, d: L.moe_dims, device="cuda", transposed: bool = False):
         self.d = d
         dt = torch.bfloat16
         P, E, D, F = d.T * d.top_k, d.E, d.D, d.F
         nm = 2 if d.act == L.MOE_ACT_SWIGLU else 1
         f32 = dict(dtype=torch.float32, device=device)
         self.pre = torch.empty((P, nm * F), dtype=dt, device=device)
-        self.w13t = torch.empty((E, D, nm * F), dtype=dt, device=device)
-        self.w2t = torch.empty((E, F, D), dtype=dt, device=device)
+        self.w13t = torch.empty((E, D, nm * F), dtype=dt, device=device) if transposed else None
+        self.w2t = torch.empty((E, F, D), dtype=dt, device=device) if transposed else None
         self.dy_perm = torch.empty((P, D), dtype=dt, device=device)
         self.dgate = torch.empty(P, **f32)
         self.da = torch.empty((P, nm * F), dtype=dt, device=device)
@@ -172,14 +174,17 @@ def forward_train(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, bias, 
 
 
 def backward(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, dy, stream=None, transpose_weights=None):
-    """The backward as one call of the library's executor (``transpose_weights``: (w1, w3, w2) to rebuild
-    bw.w13t / bw.w2t first, as after a weight update). Gradients land in bw.dx, bw.dw_gate, bw.dbias,
-    bw.dw1, bw.dw3, bw.dw2."""
+    """The backward as one call of the library's executor. ``transpose_weights``: the forward's (w1, w3,
+    w2); the data-gradient GEMMs read them directly, or, with BackwardBuffers(transposed=True), they are
+    transposed into bw.w13t / bw.w2t first (as after a weight update; None reuses the copies). Gradients
+    land in bw.dx, bw.dw_gate, bw.dbias, bw.dw1, bw.dw3, bw.dw2."""
     a = L.moe_backward_args()
     a.x, a.w_gate, a.dy = _ptr(x), _ptr(w_gate), _ptr(dy)
+    if bw.w13t is None and transpose_weights is None:
+        raise ValueError("backward without transposed weight copies needs the weights (w1, w3, w2)")
     if transpose_weights is not None:
         a.w1, a.w3, a.w2 = (_ptr(t) for t in transpose_weights)
-        a.refresh_weights = 1
+        a.refresh_weights = 1 if bw.w13t is not None else 0
     for n in ("logits", "topk_idx", "topk_gate", "expert_offsets", "pair_to_row", "row_to_pair", "x_perm", "h",
               "y_perm"):
         setattr(a, n, _ptr(getattr(buf, n)))

@@ -370,6 +370,15 @@ int moe_expert_ffn_down_backward(const moe_dims* d, const void* dy_perm, const i
 int moe_expert_ffn_up_backward(const moe_dims* d, const void* da, const int32_t* expert_offsets,
                                const void* w13t, void* dx_perm, hipStream_t stream);
 
+/* The two data-gradient GEMMs on the weights as the forward keeps them (w2 [E,D,F]; w1, w3 [E,F,D]),
+ * with no transposed copies: the kernels load K-major weight slices and transpose them in the LDS
+ * reads. Same arguments and results, bit for bit, as moe_expert_ffn_down_backward /
+ * moe_expert_ffn_up_backward on moe_transpose_weights' output; w3 may be NULL for MOE_ACT_GELU. */
+int moe_expert_ffn_down_backward_w(const moe_dims* d, const void* dy_perm, const int32_t* expert_offsets,
+                                   const void* w2, const void* pre, void* da, hipStream_t stream);
+int moe_expert_ffn_up_backward_w(const moe_dims* d, const void* da, const int32_t* expert_offsets, const void* w1,
+                                 const void* w3, void* dx_perm, hipStream_t stream);
+
 /* Router backward: dl [T, E] float32 out (0 where a logit gets no gradient), dw_gate [E, D] float32
  * out, dbias [E] float32 out or NULL (then ws may be NULL). logits: the forward's float32 logits;
  * topk_gate: the forward's gates. ws: moe_workspace_size(MOE_STAGE_ROUTER_BWD) bytes.
@@ -405,8 +414,10 @@ int moe_expert_wgrad(const moe_dims* d, const void* a_t, const void* b_t, const 
 
 /* The whole backward in order (the steps above), from one argument block. Buffers as the step entry
  * points take them; `ld` = the row length of the transposed wgrad operands (>= moe_wgrad_ld()).
- * refresh_weights != 0: rebuild w13t / w2t from w1, w3, w2 first (after a weight update). For a
- * layer with a capacity factor, dW_g takes the dense form (the forward's layout is not dropless). */
+ * w13t and w2t both NULL: the data-gradient GEMMs read w1, w3, w2 directly (the _w entry points;
+ * refresh_weights is ignored). Otherwise refresh_weights != 0 rebuilds w13t / w2t from w1, w3, w2
+ * first (after a weight update). For a layer with a capacity factor, dW_g takes the dense form (the
+ * forward's layout is not dropless). */
 typedef struct moe_backward_args {
   const void* x; const void* w_gate; const void* w1; const void* w3; const void* w2;
   const float* logits; const int32_t* topk_idx; const float* topk_gate;

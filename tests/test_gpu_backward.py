@@ -259,7 +259,7 @@ def test_native_backward_equals_the_steps(name):
     inp = W.make_inputs(cfg, "cuda")
     d = M.dims_from_config(cfg)
     buf = M.MoELayerBuffers(d, device="cuda", logits=True)
-    bw = M.BackwardBuffers(d, device="cuda")
+    bw = M.BackwardBuffers(d, device="cuda", transposed=True)
     M.forward_train(buf, bw, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
     g = torch.Generator(device="cuda")
     g.manual_seed(9)
