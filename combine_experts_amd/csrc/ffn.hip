@@ -563,20 +563,28 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
   if (nk > 0) gemm_kloop<GMB, false>(acc, lds, src, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
+  // the tile goes out through LDS: each wave stages its 32-row blocks (32 x 64 floats) in the ring slot
+  // the last stage did not read and stores 256-byte row pieces, 16 lanes per row, instead of 16-byte
+  // pieces of 32 rows per instruction
+  constexpr int SROW = 64 + 4;  // staging row stride (floats; rows stay 16-byte aligned)
+  float* stg = reinterpret_cast<float*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROW;
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
-    const int m = m0 + (2 * i + wm) * 32 + lane % 32;
-    if (m >= M) continue;
-    float* orow = m < split ? out0 + ((size_t)g * split + m) * N : out1 + ((size_t)g * (M - split) + (m - split)) * N;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = n0 + wn * 64 + j * 32 + 8 * q + 4 * (lane / 32);
-        if (c >= N) continue;
-        *reinterpret_cast<f32x4*>(orow + c) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                                    acc[i][j][4 * q + 3]};
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(stg + (lane % 32) * SROW + j * 32 + 8 * q + 4 * (lane / 32)) =
+            f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+#pragma unroll
+    for (int rr = 0; rr < 32; rr += MOE_WAVE / 16) {
+      const int r2 = rr + lane / 16, c2 = (lane % 16) * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r2 * SROW + c2);
+      const int m = m0 + (2 * i + wm) * 32 + r2, c = n0 + wn * 64 + c2;
+      if (m >= M || c >= N) continue;
+      float* orow = m < split ? out0 + ((size_t)g * split + m) * N : out1 + ((size_t)g * (M - split) + (m - split)) * N;
+      *reinterpret_cast<f32x4*>(orow + c) = v;
+    }
   }
 }
 
