@@ -17,6 +17,8 @@
 // The [64 x E] float32 logit tile then goes to LDS, and each wave selects for its 16 tokens:
 // group scores (if limited), then k rounds of a wave-wide argmax on (value, -index), so exact
 // ties go to the lower expert index.
+#include <atomic>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -604,11 +606,17 @@ hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
   if (dtype == MOE_BF16) {
     const size_t lds_w = (size_t)kDepth * epad * kKC * sizeof(bf16_t);
     const size_t lds = lds_w > lds_logits ? lds_w : lds_logits;
-    // dynamic LDS above the default 64 KB needs the per-kernel limit raised (once per process)
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&route_kernel<bf16_t, NT, BAL>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)lds);
-    if (attr != hipSuccess) return attr;
+    // dynamic LDS above the default 64 KB needs the per-kernel limit raised, once per device
+    static std::atomic<unsigned long long> raised{0};  // one bit per device
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(raised.load(std::memory_order_acquire) & bit)) {
+      const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_kernel<bf16_t, NT, BAL>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (attr != hipSuccess) return attr;
+      raised.fetch_or(bit, std::memory_order_release);
+    }
     hipLaunchKernelGGL((route_kernel<bf16_t, NT, BAL>), dim3(blocks), dim3(256), lds, s, (const bf16_t*)a.x,
                        (const bf16_t*)a.w_gate, a.bias, a.select_bias, a.topk_idx, a.topk_gate, a.logits,
                        a.prob_partials, a.T, a.D, a.E, a.k, a.n_groups, a.topk_groups, a.gate);
