@@ -361,6 +361,19 @@ def main(argv=None):
     pz.record(stream)
     torch.cuda.synchronize()
     permute_ms = pa.elapsed_time(pz) / 20
+    # the same step captured once in a HIP graph and replayed (one launch per step)
+    gl = M.GraphLayer(d, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], device=dev)
+    for _ in range(args.warmup):
+        gl.replay()
+    ga, gz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ga.record(stream)
+    for _ in range(args.steps):
+        gl.replay()
+    gz.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gz) / args.steps
+    del gl
 
     N = int(buf.expert_offsets[-1].item())
     counts = buf.expert_counts.cpu()
@@ -403,6 +416,7 @@ def main(argv=None):
     log(f"[bench] N={N} kept rows, max/mean expert count {float(counts.max()) / float(counts.float().mean()):.2f}")
     for s in STAGES:
         log(f"[bench]   {s:9s} {stage_ms[s] * 1e3:9.1f} us")
+    log(f"[bench] step as a HIP graph replay: {graph_ms * 1e3:.1f} us")
     log(f"[bench] permute {permute_gbs:.0f} GB/s, combine {combine_gbs:.0f} GB/s, "
         f"FFN {ffn_tflops:.0f} TFLOP/s ({ffn_tflops / peak * 100:.1f}% of peak)")
 
@@ -480,6 +494,8 @@ def main(argv=None):
         "layer_roofline": {"bound_ms": round(layer_bound, 4), "frac": round(layer_bound / ms_per_step, 4),
                            "note": "sum of the stages' spec-peak bounds over the measured step"},
         "permute": "inside ffn_up (rows gathered from x by the GEMM's loads)",
+        "graph": {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
+                  "note": "the same step captured once in a HIP graph and replayed"},
         "extra_stage_ms": {"permute_standalone": round(permute_ms, 4), **{s: round(v, 4) for s, v in extra_ms.items()}},
         "cluster_emulation": cluster,
         "padded_capacity": padded,

@@ -19,4 +19,5 @@ from ._lib import (  # noqa: F401
     MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL, MOE_ACT_SWIGLU, MOE_ACT_GELU,
     MOE_F32, MOE_BF16, MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS,
 )
-from .layer import MoELayerBuffers, forward, LayerExecutor, BackwardBuffers, forward_train, backward  # noqa: F401
+from .layer import (MoELayerBuffers, forward, LayerExecutor, GraphLayer, BackwardBuffers, forward_train,  # noqa: F401
+                    backward)

@@ -129,6 +129,31 @@ class LayerExecutor:
         return self.y
 
 
+class GraphLayer:
+    """The layer forward captured once in a HIP graph and replayed: one graph launch per step instead
+    of the eight to ten kernel launches, which is most of the time of a small layer. Every replay
+    reads the tensors given here (write new inputs into them in place) and writes ``self.buf.y``.
+    The library allocates, synchronises and clears nothing inside the step, so the whole step
+    captures; the first (eager) call, made before capture, also raises the router's LDS limit."""
+
+    def __init__(self, d: L.moe_dims, x, w_gate, bias, w1, w3, w2, device="cuda", gather: bool = True):
+        self.buf = MoELayerBuffers(d, device=device, x_perm=not gather)
+        self.args = (x, w_gate, bias, w1, w3, w2)
+        side = torch.cuda.Stream(device=device)
+        side.wait_stream(torch.cuda.current_stream(device))
+        with torch.cuda.stream(side):
+            forward(self.buf, *self.args)
+        torch.cuda.current_stream(device).wait_stream(side)
+        torch.cuda.synchronize(device)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            forward(self.buf, *self.args)
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.buf.y
+
+
 class BackwardBuffers:
     """Buffers of one training step's backward for dims d (bf16): saved pre-activations, the backward's
     activations, transposed wgrad operands and float32 gradients. transposed=True also keeps transposed
