@@ -134,14 +134,17 @@ __device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ x, const 
 __device__ __forceinline__ void logits_f32(const float* __restrict__ x, const float* __restrict__ wg, const float* bias,
                            float* lds_logits, int epad, int T, int D, int E, int t0) {
   const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
-  for (int i = 0; i < kTokPerWave; ++i) {
+  // the wave's (token, expert) pairs spread over all lanes; each dot product in d order
+  for (int p = lane; p < kTokPerWave * epad; p += MOE_WAVE) {
+    const int i = p / epad, e = p % epad;
     const int trow = wave * kTokPerWave + i;
     const int tok = t0 + trow;
-    for (int e = lane; e < epad; e += MOE_WAVE) {
+    {
       float s = 0.f;
       if (tok < T && e < E) {
         const float* xr = x + (size_t)tok * D;
         const float* wr = wg + (size_t)e * D;
+#pragma unroll 4
         for (int d = 0; d < D; d += 4) {
           const f32x4 xv = *reinterpret_cast<const f32x4*>(xr + d);
           const f32x4 wv = *reinterpret_cast<const f32x4*>(wr + d);
