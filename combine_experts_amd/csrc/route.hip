@@ -6,15 +6,15 @@
 // All-to-All", section on fighting back) restricts a token to its best groups before the
 // per-expert choice.
 //
-// One block = 4 waves = 64 tokens; all E (<= 256) experts of a token stay in one block, so the
+// One block = 8 waves = 64 tokens; all E (<= 256) experts of a token stay in one block, so the
 // selection needs no second pass over HBM.
-//   bf16: matrix cores (v_mfma_f32_16x16x32_bf16) with float32 accumulation. Each wave owns 16
-//         tokens; the block streams 64-wide K slices of W_g for all experts through an LDS ring
-//         (direct global->LDS loads, 16-byte chunks XOR-swizzled against bank conflicts) while x
-//         fragments stream from HBM into registers, four slices in flight (the step is bound by
-//         HBM bandwidth on x, so latency must be covered by depth, not by compute).
+//   bf16: matrix cores (v_mfma_f32_16x16x32_bf16) with float32 accumulation. The block streams
+//         64-wide K slices of its 64 x rows and of W_g (all experts) into a ring of LDS stages with
+//         direct global->LDS loads (16-byte chunks, XOR-swizzled against bank conflicts), several
+//         slices in flight; each wave multiplies a 32-token x 64-expert piece of the tile from LDS.
+//         Only direct loads are in flight, so every wait is an explicit count.
 //   fp32: plain FMA dot products (the small fp32 workload only).
-// The [64 x E] float32 logit tile then goes to LDS, and each wave selects for its 16 tokens:
+// The [64 x E] float32 logit tile then goes to LDS, and each wave selects for its 8 tokens:
 // group scores (if limited), then k rounds of a wave-wide argmax on (value, -index), so exact
 // ties go to the lower expert index.
 #include <atomic>
@@ -25,7 +25,9 @@ namespace moe {
 namespace {
 
 constexpr int kTokPerBlock = kRouteTokPerBlock;
-constexpr int kTokPerWave = 16;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * MOE_WAVE;
+constexpr int kTokPerWave = kTokPerBlock / kWaves;  // tokens each wave selects for
 constexpr int kKC = 64;           // K slice per pipeline stage (two MFMA k-steps of 32)
 constexpr int kMaxE = 256;
 constexpr int kMaxPerLane = kMaxE / MOE_WAVE;
@@ -39,93 +41,143 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-// Streaming K loop, kDepth slices in flight: W_g K-slices go global -> LDS directly (16 bytes per
-// lane; lane i of a load fills LDS chunk base + i) through a kDepth-slot ring; x fragments go into a
-// kDepth-deep register ring with non-temporal loads (each x element is read once; W_g stays in L2).
-// The loop is unrolled by kDepth so ring indices are compile-time. Requires D % 64 == 0.
-constexpr int kDepth = 4;
+// Workgroup barrier without __syncthreads' release fence, which waits for every load in flight
+// (the prefetched slices included). Each wave has already waited for its own loads of the slice it
+// needs; the memory clobber keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int NT>  // 16-expert MFMA column tiles; experts padded to NT*16
-__device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* bias,
-                            float* lds_logits, char* lds_raw, int T, int D, int E, int t0) {
+// Stage geometry for NT 16-expert tiles (experts padded to NT*16): one stage holds a 64-wide K slice
+// of the block's 64 x rows (512 chunks of 16 bytes) and of all padded W_g rows (128*NT chunks),
+// padded to a whole number of chunks per thread so every thread issues the same number of loads.
+template <int NT>
+struct RouteStage {
+  static constexpr int XCH = kTokPerBlock * (kKC / 8);
+  static constexpr int CH = XCH + NT * 16 * (kKC / 8);
+  static constexpr int LPT = (CH + kThreads - 1) / kThreads;  // direct loads per thread per stage
+  static constexpr int PCH = LPT * kThreads;                   // padded chunks per stage
+  static constexpr int DEPTH = NT >= 16 ? 4 : 6;               // ring slots
+  static constexpr size_t BYTES = (size_t)DEPTH * PCH * 16;
+  // waves: WT token groups x WE expert groups; each wave TT 16-token tiles x TE 16-expert tiles
+  static constexpr int WE = NT < 4 ? NT : 4;
+  static constexpr int WT = (kWaves / WE) < 4 ? kWaves / WE : 4;
+  static constexpr int TT = 4 / WT;
+  static constexpr int TE = NT / WE;
+};
+
+// Logit tile of the block: the K loop over DEPTH ring slots, DEPTH-1 slices in flight. Every
+// iteration issues one slice (past the end, the last slice again into the slot just freed, never
+// read), so the number of loads behind slice kc is fixed. Requires D % 64 == 0.
+template <int NT>
+__device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                            const float* bias, float* lds_logits, char* lds_raw, int T, int D,
+                                            int E, int t0) {
+  using S = RouteStage<NT>;
   constexpr int epad = NT * 16;
-  constexpr int STAGE = epad * (kKC / 8);        // 16-byte chunks per slice
-  constexpr int LPT = (STAGE + 255) / 256;       // direct loads per thread per slice
-  constexpr int PER_STAGE = LPT + 2;             // vector-memory instructions per slice per wave
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / MOE_WAVE);
   const int lane = tid % MOE_WAVE;
-  bf16x8* wbuf = reinterpret_cast<bf16x8*>(lds_raw);  // [kDepth][STAGE]
+  bf16x8* ring = reinterpret_cast<bf16x8*>(lds_raw);  // [DEPTH][PCH]
 
-  const bf16_t* wsrc[LPT];
+  // source of each of this thread's loads (chunk slot i*kThreads + tid of a stage)
+  const bf16_t* src[S::LPT];
 #pragma unroll
-  for (int i = 0; i < LPT; ++i) {
-    const int slot = i * 256 + wave * MOE_WAVE + lane;
-    const int row = slot / (kKC / 8), ch = swz(row, slot % (kKC / 8));
-    wsrc[i] = wg + (size_t)(row < E ? row : E - 1) * D + ch * 8;  // padded experts reuse a real row
+  for (int i = 0; i < S::LPT; ++i) {
+    const int slot = i * kThreads + tid;
+    if (slot < S::XCH) {
+      const int row = slot / (kKC / 8), ch = swz(row, slot % (kKC / 8));
+      const int tok = t0 + row;
+      src[i] = x + (size_t)(tok < T ? tok : T - 1) * D + ch * 8;  // rows past T: values unused
+    } else {
+      const int ws = slot < S::CH ? slot - S::XCH : 0;  // padding slots reload chunk 0 of row 0
+      const int row = ws / (kKC / 8), ch = swz(row, ws % (kKC / 8));
+      src[i] = wg + (size_t)(row < E ? row : E - 1) * D + ch * 8;  // padded experts reuse a real row
+    }
   }
-  const int r = lane % 16, q = lane / 16;          // MFMA row / k-quarter of this lane
-  const int tok = t0 + wave * kTokPerWave + r;
-  const bf16_t* xrow = x + (size_t)(tok < T ? tok : T - 1) * D + q * 16;  // rows past T: values unused
-  const int n_kc = D / kKC;
-  bf16x8 a[kDepth][2];
-
-  // stage kc -> ring slot kc % kDepth (W) and register set kc % kDepth (x)
   auto issue = [&](int kc, int slot) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i)
-      if (i * 256 + wave * MOE_WAVE < STAGE)  // wave-uniform
-        __builtin_amdgcn_global_load_lds((const void*)(wsrc[i] + kc * kKC),
-                                         (__attribute__((address_space(3))) void*)(wbuf + slot * STAGE + i * 256 +
-                                                                                   wave * MOE_WAVE),
-                                         16, 0, 0);
-    a[slot][0] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(xrow + kc * kKC));
-    a[slot][1] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(xrow + kc * kKC + 8));
+    for (int i = 0; i < S::LPT; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(src[i] + kc * kKC),
+                                       (__attribute__((address_space(3))) void*)(ring + slot * S::PCH + i * kThreads +
+                                                                                 wave * MOE_WAVE),
+                                       16, 0, 0);
   };
 
-  f32x4 acc[NT];
+  // this wave's piece: token tiles [wt*TT, +TT), expert tiles [we*TE, +TE); waves past WT*WE idle
+  const bool active = wave < S::WT * S::WE;
+  const int wt = wave / S::WE, we = wave % S::WE;
+  const int r = lane % 16, q = lane / 16;  // MFMA row / k-quarter of this lane
+  int xoff[S::TT][2], woff[S::TE][2];
 #pragma unroll
-  for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int a = 0; a < S::TT; ++a) {
+    const int row = (wt * S::TT + a) * 16 + r;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) xoff[a][s2] = row * (kKC / 8) + swz(row, q * 2 + s2);
+  }
+#pragma unroll
+  for (int b = 0; b < S::TE; ++b) {
+    const int row = (we * S::TE + b) * 16 + r;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) woff[b][s2] = S::XCH + row * (kKC / 8) + swz(row, q * 2 + s2);
+  }
+  f32x4 acc[S::TT][S::TE];
+#pragma unroll
+  for (int a = 0; a < S::TT; ++a)
+#pragma unroll
+    for (int b = 0; b < S::TE; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int n_kc = D / kKC;
 #pragma unroll
-  for (int st = 0; st < kDepth - 1; ++st)
-    if (st < n_kc) issue(st, st);
-  for (int kc0 = 0; kc0 < n_kc; kc0 += kDepth) {
+  for (int st = 0; st < S::DEPTH - 1; ++st) issue(min(st, n_kc - 1), st);
+  for (int kc0 = 0; kc0 < n_kc; kc0 += S::DEPTH) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
+    for (int u = 0; u < S::DEPTH; ++u) {
       const int kc = kc0 + u;
       if (kc < n_kc) {
-        // slice kc landed (this wave's W loads; x registers are waited on by the compiler) ...
-        const int later = n_kc - 1 - kc;  // slices issued after kc, at most kDepth - 2
-        if (later >= kDepth - 2) wait_vmcnt<(kDepth - 2) * PER_STAGE>();
-        else if (later == 1) wait_vmcnt<PER_STAGE>();
-        else wait_vmcnt<0>();
-        __syncthreads();  // ... for every wave; and every wave is done reading slot (kc-1) % kDepth
-        if (kc + kDepth - 1 < n_kc) issue(kc + kDepth - 1, (u + kDepth - 1) % kDepth);
-        const bf16x8* wb = wbuf + u * STAGE;
-        // lane (r, q) supplies K elements [q*16, q*16+16) of this slice as two 8-wide MFMA fragments
+        wait_vmcnt<(S::DEPTH - 2) * S::LPT>();  // this wave's loads of slice kc landed ...
+        lds_barrier();  // ... and everyone's; everyone is also done reading slot (kc-1) % DEPTH
+        issue(min(kc + S::DEPTH - 1, n_kc - 1), (u + S::DEPTH - 1) % S::DEPTH);
+        if (active) {
+          // lane (r, q) supplies K elements [q*16, q*16+16) of the slice as two 8-wide fragments;
+          // all of the slice's fragments are read first, then the MFMAs run (s2 = 0, then 1, for
+          // every output, in slice order)
+          const bf16x8* st = ring + u * S::PCH;
+          bf16x8 xa[S::TT][2], wb[S::TE][2];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const int row = nt * 16 + r;
+          for (int a = 0; a < S::TT; ++a)
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 b = wb[row * (kKC / 8) + swz(row, q * 2 + s2)];
-            acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][s2], b, acc[nt], 0, 0, 0);
-          }
+            for (int s2 = 0; s2 < 2; ++s2) xa[a][s2] = st[xoff[a][s2]];
+#pragma unroll
+          for (int b = 0; b < S::TE; ++b)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) wb[b][s2] = st[woff[b][s2]];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int a = 0; a < S::TT; ++a)
+#pragma unroll
+              for (int b = 0; b < S::TE; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[a][s2], wb[b][s2], acc[a][b], 0, 0, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * (S::TT + S::TE), 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * S::TT * S::TE, 0);
         }
       }
     }
   }
-  __syncthreads();  // all waves done with the ring before the logit tile reuses the memory
-  // acc[nt][i]: token row (lane/16)*4 + i of this wave, expert nt*16 + lane%16
+  wait_vmcnt<0>();  // the redundant tail loads land before the ring memory is reused
+  lds_barrier();    // all waves done with the ring before the logit tile reuses the memory
+  // acc[a][b][i]: token row (wt*TT + a)*16 + (lane/16)*4 + i, expert (we*TE + b)*16 + lane%16
+  if (active) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int e = nt * 16 + (lane % 16);
-    const float bv = (bias != nullptr && e < E) ? bias[e] : 0.f;
+    for (int b = 0; b < S::TE; ++b) {
+      const int e = (we * S::TE + b) * 16 + (lane % 16);
+      const float bv = (bias != nullptr && e < E) ? bias[e] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int trow = wave * kTokPerWave + (lane / 16) * 4 + i;
-      lds_logits[trow * epad + e] = acc[nt][i] + bv;
+      for (int a = 0; a < S::TT; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int trow = (wt * S::TT + a) * 16 + (lane / 16) * 4 + i;
+          lds_logits[trow * epad + e] = acc[a][b][i] + bv;
+        }
     }
   }
 }
@@ -521,7 +573,7 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
 
 // BAL = false is the plain router: the selection bias and the probability sums are compiled out.
 template <typename T, int NT, bool BAL>
-__global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, const T* __restrict__ wg,
+__global__ void __launch_bounds__(kThreads) route_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                     const float* __restrict__ bias, const float* __restrict__ sbias_,
                                                     int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
                                                     float* __restrict__ logits, float* __restrict__ prob_partials_,
@@ -594,9 +646,11 @@ __global__ void __launch_bounds__(256) route_kernel(const T* __restrict__ x, con
   if (want_p) {
     // block partial, waves summed in a fixed order: the result does not depend on scheduling
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x)
-      prob_partials[(size_t)blockIdx.x * E + e] =
-          ((wsum[e] + wsum[epad + e]) + wsum[2 * epad + e]) + wsum[3 * epad + e];
+    for (int e = threadIdx.x; e < E; e += blockDim.x) {
+      float sum = wsum[e];
+      for (int w = 1; w < kWaves; ++w) sum += wsum[w * epad + e];
+      prob_partials[(size_t)blockIdx.x * E + e] = sum;
+    }
   }
 }
 
@@ -604,10 +658,10 @@ template <int NT, bool BAL>
 hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
   constexpr int epad = NT * 16;
   const int blocks = (a.T + kTokPerBlock - 1) / kTokPerBlock;
-  // logit tile [64 x epad] plus four per-wave probability rows
-  const size_t lds_logits = (size_t)(kTokPerBlock + 4) * epad * sizeof(float);
+  // logit tile [64 x epad] plus one probability row per wave
+  const size_t lds_logits = (size_t)(kTokPerBlock + kWaves) * epad * sizeof(float);
   if (dtype == MOE_BF16) {
-    const size_t lds_w = (size_t)kDepth * epad * kKC * sizeof(bf16_t);
+    const size_t lds_w = RouteStage<NT>::BYTES;
     const size_t lds = lds_w > lds_logits ? lds_w : lds_logits;
     // dynamic LDS above the default 64 KB needs the per-kernel limit raised, once per device
     static std::atomic<unsigned long long> raised{0};  // one bit per device
@@ -620,11 +674,11 @@ hipError_t launch_route_nt(const RouteArgs& a, int dtype, hipStream_t s) {
       if (attr != hipSuccess) return attr;
       raised.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((route_kernel<bf16_t, NT, BAL>), dim3(blocks), dim3(256), lds, s, (const bf16_t*)a.x,
+    hipLaunchKernelGGL((route_kernel<bf16_t, NT, BAL>), dim3(blocks), dim3(kThreads), lds, s, (const bf16_t*)a.x,
                        (const bf16_t*)a.w_gate, a.bias, a.select_bias, a.topk_idx, a.topk_gate, a.logits,
                        a.prob_partials, a.T, a.D, a.E, a.k, a.n_groups, a.topk_groups, a.gate);
   } else {
-    hipLaunchKernelGGL((route_kernel<float, NT, BAL>), dim3(blocks), dim3(256), lds_logits, s, (const float*)a.x,
+    hipLaunchKernelGGL((route_kernel<float, NT, BAL>), dim3(blocks), dim3(kThreads), lds_logits, s, (const float*)a.x,
                        (const float*)a.w_gate, a.bias, a.select_bias, a.topk_idx, a.topk_gate, a.logits,
                        a.prob_partials, a.T, a.D, a.E, a.k, a.n_groups, a.topk_groups, a.gate);
   }
