@@ -12,7 +12,7 @@ import torch
 import combine_experts_amd as M
 import oracle as O
 import workloads as W
-from _parity import TOL_Y, f64, rel_err_rows
+from tests._parity import TOL_Y, f64, rel_err_rows
 
 pytestmark = pytest.mark.gpu
 
