@@ -216,6 +216,43 @@ __device__ __forceinline__ bool better(float v, int e, float ov, int oe) {
   return ov > v || (ov == v && oe < e);
 }
 
+// The same register of another lane of this lane's 16-lane row, through DPP (a modifier of a VALU
+// move: no LDS round trip, unlike a general shuffle). Applied in the order xor 1, xor 2 (quad
+// permutations), mirror within 8 lanes, mirror within 16, each step pairs a lane with one of the
+// other half of the group merged so far, whose lanes all hold the same value by then: a butterfly
+// over the row for any associative, commutative, exact reduction (max, argmax, merge of top lists).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& be) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oe = dpp_i<CTRL>(be);
+  if (better(bv, be, ov, oe)) {
+    bv = ov;
+    be = oe;
+  }
+}
+// (value, -index) maximum over the 16-lane row, in every lane of the row
+__device__ __forceinline__ void argmax16(float& bv, int& be) {
+  argmax_step<kDppXor1>(bv, be);
+  argmax_step<kDppXor2>(bv, be);
+  argmax_step<kDppHalfMirror>(bv, be);
+  argmax_step<kDppMirror>(bv, be);
+}
+__device__ __forceinline__ float max16(float m) {
+  m = fmaxf(m, dpp_f<kDppXor1>(m));
+  m = fmaxf(m, dpp_f<kDppXor2>(m));
+  m = fmaxf(m, dpp_f<kDppHalfMirror>(m));
+  return fmaxf(m, dpp_f<kDppMirror>(m));
+}
+
 __device__ __forceinline__ float sigmoidf_(float v) { return 1.f / (1.f + expf(-v)); }
 
 // ---- selection and gates for one token ------------------------------------------------------------
@@ -439,8 +476,7 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NT; ++i) m = fmaxf(m, v[i]);
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, MOE_WAVE));
+    m = max16(m);
     float num[NT], z = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
@@ -458,49 +494,65 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
     const int gsize = E / n_groups;
     const int lpg = gsize / NT;                   // lanes per group
     const int per = max(1, k / topk_groups);      // members summed per group (<= 8)
-    // this lane's `per` best member scores, descending
-    float best[8];
+    // Group score: the sum of the group's `per` best member scores, in descending order. Members are
+    // ranked by the logit itself where the score is its sigmoid (monotonic: the same members, the
+    // same order), so only the chosen ones pass through the sigmoid. P bounds `per` at compile time.
+    const bool sig_after = !has_sb && gate == MOE_GATE_SIGMOID_TOPK;
+    auto group_score = [&](auto pc) -> float {
+      constexpr int P = decltype(pc)::value;
+      float best[P];  // this lane's `per` best, descending
 #pragma unroll
-    for (int j = 0; j < 8; ++j) best[j] = -INFINITY;
+      for (int j = 0; j < P; ++j) best[j] = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      float sv = has_sb ? key[i] : ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(v[i]) : v[i]);
+      for (int i = 0; i < NT; ++i) {
+        float sv = has_sb ? key[i] : v[i];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j < per && sv > best[j]) {
-          const float t = best[j];
-          best[j] = sv;
-          sv = t;
+        for (int j = 0; j < P; ++j) {
+          if ((P <= 2 || j < per) && sv > best[j]) {
+            const float t = best[j];
+            best[j] = sv;
+            sv = t;
+          }
         }
       }
-    }
-    // merge sorted lists across the lanes of the group
-    for (int off = 1; off < lpg; off <<= 1) {
-      float other[8];
+      // merge sorted lists across the lanes of the group (lpg lanes: 1, 2, 4, 8 or 16)
+      auto merge = [&](auto ctrl) {
+        constexpr int C = decltype(ctrl)::value;
+        float other[P];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) other[j] = __shfl_xor(best[j], off, MOE_WAVE);
-      float merged[8];
-      int ia = 0, ib = 0;
+        for (int j = 0; j < P; ++j) other[j] = dpp_f<C>(best[j]);
+        float merged[P];
+        int ia = 0, ib = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float a = -INFINITY, b = -INFINITY;
+        for (int j = 0; j < P; ++j) {
+          float a = -INFINITY, b = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          if (q == ia) a = best[q];
-          if (q == ib) b = other[q];
+          for (int q = 0; q < P; ++q) {
+            if (q == ia) a = best[q];
+            if (q == ib) b = other[q];
+          }
+          const bool take_a = a >= b;
+          merged[j] = take_a ? a : b;
+          ia += take_a ? 1 : 0;
+          ib += take_a ? 0 : 1;
         }
-        const bool take_a = a >= b;
-        merged[j] = take_a ? a : b;
-        ia += take_a ? 1 : 0;
-        ib += take_a ? 0 : 1;
-      }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) best[j] = merged[j];
-    }
-    float gs = 0.f;  // group score, in every lane of the group (summed in descending order)
+        for (int j = 0; j < P; ++j) best[j] = merged[j];
+      };
+      if (lpg > 1) merge(std::integral_constant<int, kDppXor1>{});
+      if (lpg > 2) merge(std::integral_constant<int, kDppXor2>{});
+      if (lpg > 4) merge(std::integral_constant<int, kDppHalfMirror>{});
+      if (lpg > 8) merge(std::integral_constant<int, kDppMirror>{});
+      float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < per) gs += best[j];
+      for (int j = 0; j < P; ++j)
+        if (j < per) sum += sig_after ? sigmoidf_(best[j]) : best[j];
+      return sum;
+    };
+    // group score, in every lane of the group
+    const float gs = per == 1   ? group_score(std::integral_constant<int, 1>{})
+                     : per == 2 ? group_score(std::integral_constant<int, 2>{})
+                                : group_score(std::integral_constant<int, 8>{});
     const int my_g = L / lpg;
     int rank = 0;
     for (int g = 0; g < n_groups; ++g) {
@@ -526,15 +578,7 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
         be = e;
       }
     }
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, MOE_WAVE);
-      const int oe = __shfl_xor(be, off, MOE_WAVE);
-      if (better(bv, be, ov, oe)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    argmax16(bv, be);
 #pragma unroll
     for (int i = 0; i < NT; ++i)
       if (L * NT + i == be) ok[i] = false;
@@ -552,8 +596,7 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < NT; ++i) m = fmaxf(m, v[i]);
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, MOE_WAVE));
+    m = max16(m);
     float z = 0.f;
 #pragma unroll
     for (int i = 0; i < NT; ++i) z += expf(v[i] - m);
