@@ -356,7 +356,8 @@ __global__ void __launch_bounds__(256) group_transpose_kernel(const T* __restric
     const int cl = q / CPR, jc = q % CPR;
     const int c = c0 + cl;
     if (c < C)
-      *reinterpret_cast<u32x4*>(dst + (size_t)c * ld + j0 + jc * VN) = *reinterpret_cast<const u32x4*>(&tile[cl][jc * VN]);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&tile[cl][jc * VN]),
+                                  reinterpret_cast<u32x4*>(dst + (size_t)c * ld + j0 + jc * VN));
   }
 }
 

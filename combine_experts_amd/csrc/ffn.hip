@@ -583,7 +583,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
       const int m = m0 + (2 * i + wm) * 32 + r2, c = n0 + wn * 64 + c2;
       if (m >= M || c >= N) continue;
       float* orow = m < split ? out0 + ((size_t)g * split + m) * N : out1 + ((size_t)g * (M - split) + (m - split)) * N;
-      *reinterpret_cast<f32x4*>(orow + c) = v;
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(orow + c));  // streamed: keeps L2 for the operands
     }
   }
 }
