@@ -228,6 +228,75 @@ __global__ void __launch_bounds__(256) router_wgrad_grouped_kernel(const T* __re
   }
 }
 
+// backward_combine_kernel for k <= KMAX: the token's rows, gates and the k dot products stay in
+// registers, and for each group of U chunks per lane the dy chunks and all k y_perm chunks are loaded
+// before the first FMA (k*U + U loads in flight per lane). Each lane accumulates its dot products over
+// its chunks in the same order as backward_combine_kernel, so the same bits.
+template <typename T, int KMAX, int U>
+__global__ void __launch_bounds__(256) backward_combine_k_kernel(const T* __restrict__ dy, const int32_t* __restrict__ p2r,
+                                                                 const float* __restrict__ gate,
+                                                                 const T* __restrict__ yp, T* __restrict__ dyp,
+                                                                 float* __restrict__ dgate, int T_, int D, int k) {
+  constexpr int VN = 16 / sizeof(T);
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  const int nch = D / VN;
+  for (int t = blockIdx.x * 4 + wave; t < T_; t += gridDim.x * 4) {
+    const u32x4* dyr = reinterpret_cast<const u32x4*>(dy + (size_t)t * D);
+    int rows[KMAX];
+    float g[KMAX], dot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? p2r[(size_t)t * k + j] : -1;
+      g[j] = (rows[j] >= 0) ? gate[(size_t)t * k + j] : 0.f;
+      dot[j] = 0.f;
+    }
+    for (int c0 = 0; c0 < nch; c0 += MOE_WAVE * U) {
+      u32x4 rv[U], ry[KMAX][U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        rv[u] = c < nch ? dyr[c] : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          ry[j][u] = (rows[j] >= 0 && c < nch) ? reinterpret_cast<const u32x4*>(yp + (size_t)rows[j] * D)[c]
+                                                : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (rows[j] < 0) continue;
+        u32x4* dr = reinterpret_cast<u32x4*>(dyp + (size_t)rows[j] * D);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          if (c >= nch) continue;
+          const T* v = reinterpret_cast<const T*>(&rv[u]);
+          const T* w = reinterpret_cast<const T*>(&ry[j][u]);
+          u32x4 ro;
+          T* o = reinterpret_cast<T*>(&ro);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) {
+            const float f = ld_f32(v + i);
+            o[i] = st_cvt<T>(g[j] * f);
+            dot[j] = fmaf(f, ld_f32(w + i), dot[j]);
+          }
+          dr[c] = ro;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      if (j >= k) break;
+      float d = dot[j];
+      for (int off = MOE_WAVE / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off, MOE_WAVE);
+      if (lane == 0) dgate[(size_t)t * k + j] = rows[j] >= 0 ? d : 0.f;
+    }
+  }
+}
+
 // dx[t] = sum over kept slots of dx_perm[row] + sum_e dl[t, e] W_g[e] (the selected experts, or all E
 // under full-softmax gates), float32 sums in slot / expert order, one rounding. One wave per token,
 // 16-byte chunks.
@@ -267,6 +336,70 @@ __global__ void __launch_bounds__(256) backward_dx_kernel(const T* __restrict__ 
 #pragma unroll
       for (int i = 0; i < VN; ++i) o[i] = st_cvt<T>(acc[i]);
       reinterpret_cast<u32x4*>(dx + (size_t)t * D)[c] = ro;
+    }
+  }
+}
+
+// backward_dx_kernel for k <= KMAX with the selected experts only: rows, experts and dl weights in
+// registers, and for each group of U chunks per lane the k dx_perm chunks and the k W_g chunks are
+// loaded before the sums, which run in the same order as in backward_dx_kernel (same bits).
+template <typename T, int KMAX, int U>
+__global__ void __launch_bounds__(256) backward_dx_k_kernel(const T* __restrict__ dxp, const int32_t* __restrict__ p2r,
+                                                            const int32_t* __restrict__ idx, const float* __restrict__ dl,
+                                                            const T* __restrict__ wg, T* __restrict__ dx, int T_, int D,
+                                                            int E, int k) {
+  constexpr int VN = 16 / sizeof(T);
+  const int wave = threadIdx.x / MOE_WAVE, lane = threadIdx.x % MOE_WAVE;
+  const int nch = D / VN;
+  for (int t = blockIdx.x * 4 + wave; t < T_; t += gridDim.x * 4) {
+    int rows[KMAX], ex[KMAX];
+    float w[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? p2r[(size_t)t * k + j] : -1;
+      const int e = j < k ? idx[(size_t)t * k + j] : -1;
+      ex[j] = (e >= 0 && e < E) ? e : -1;
+      w[j] = ex[j] >= 0 ? dl[(size_t)t * E + ex[j]] : 0.f;
+    }
+    for (int c0 = 0; c0 < nch; c0 += MOE_WAVE * U) {
+      u32x4 rp[KMAX][U], rw[KMAX][U];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int c = c0 + u * MOE_WAVE + lane;
+          rp[j][u] = (rows[j] >= 0 && c < nch) ? reinterpret_cast<const u32x4*>(dxp + (size_t)rows[j] * D)[c]
+                                                : u32x4{0u, 0u, 0u, 0u};
+          rw[j][u] = (ex[j] >= 0 && c < nch) ? reinterpret_cast<const u32x4*>(wg + (size_t)ex[j] * D)[c]
+                                              : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * MOE_WAVE + lane;
+        if (c >= nch) continue;
+        float acc[VN];
+#pragma unroll
+        for (int i = 0; i < VN; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (rows[j] < 0) continue;
+          const T* v = reinterpret_cast<const T*>(&rp[j][u]);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[i] += ld_f32(v + i);
+        }
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (ex[j] < 0) continue;
+          const T* v = reinterpret_cast<const T*>(&rw[j][u]);
+#pragma unroll
+          for (int i = 0; i < VN; ++i) acc[i] = fmaf(w[j], ld_f32(v + i), acc[i]);
+        }
+        u32x4 ro;
+        T* o = reinterpret_cast<T*>(&ro);
+#pragma unroll
+        for (int i = 0; i < VN; ++i) o[i] = st_cvt<T>(acc[i]);
+        reinterpret_cast<u32x4*>(dx + (size_t)t * D)[c] = ro;
+      }
     }
   }
 }
@@ -371,12 +504,25 @@ unsigned tok_grid(int T_) {
 hipError_t launch_backward_combine(const void* dy, const int32_t* p2r, const float* gate, const void* yp, void* dyp,
                                    float* dgate, int T, int D, int k, int dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (dtype == MOE_BF16)
-    hipLaunchKernelGGL(backward_combine_kernel<bf16_t>, dim3(tok_grid(T)), dim3(256), 0, s, (const bf16_t*)dy, p2r, gate,
-                       (const bf16_t*)yp, (bf16_t*)dyp, dgate, T, D, k);
-  else
-    hipLaunchKernelGGL(backward_combine_kernel<float>, dim3(tok_grid(T)), dim3(256), 0, s, (const float*)dy, p2r, gate,
-                       (const float*)yp, (float*)dyp, dgate, T, D, k);
+#define MOE_BWC_K(TT, KM, UU)                                                                                       \
+  hipLaunchKernelGGL((backward_combine_k_kernel<TT, KM, UU>), dim3(tok_grid(T)), dim3(256), 0, s, (const TT*)dy, p2r, \
+                     gate, (const TT*)yp, (TT*)dyp, dgate, T, D, k)
+  if (dtype == MOE_BF16) {
+    if (k <= 2) MOE_BWC_K(bf16_t, 2, 4);
+    else if (k <= 4) MOE_BWC_K(bf16_t, 4, 2);
+    else if (k <= 8) MOE_BWC_K(bf16_t, 8, 2);
+    else
+      hipLaunchKernelGGL(backward_combine_kernel<bf16_t>, dim3(tok_grid(T)), dim3(256), 0, s, (const bf16_t*)dy, p2r,
+                         gate, (const bf16_t*)yp, (bf16_t*)dyp, dgate, T, D, k);
+  } else {
+    if (k <= 2) MOE_BWC_K(float, 2, 4);
+    else if (k <= 4) MOE_BWC_K(float, 4, 2);
+    else if (k <= 8) MOE_BWC_K(float, 8, 2);
+    else
+      hipLaunchKernelGGL(backward_combine_kernel<float>, dim3(tok_grid(T)), dim3(256), 0, s, (const float*)dy, p2r,
+                         gate, (const float*)yp, (float*)dyp, dgate, T, D, k);
+  }
+#undef MOE_BWC_K
   return hipGetLastError();
 }
 
@@ -426,6 +572,22 @@ hipError_t launch_router_wgrad_grouped(const void* x, const float* dl, const int
 hipError_t launch_backward_dx(const void* dxp, const int32_t* p2r, const int32_t* idx, const float* dl, const void* wg,
                               void* dx, int T, int D, int E, int k, int all_experts, int dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
+#define MOE_BDX_K(TT, KM, UU)                                                                                       \
+  hipLaunchKernelGGL((backward_dx_k_kernel<TT, KM, UU>), dim3(tok_grid(T)), dim3(256), 0, s, (const TT*)dxp, p2r, idx, \
+                     dl, (const TT*)wg, (TT*)dx, T, D, E, k)
+  if (!all_experts && k <= 8) {
+    if (dtype == MOE_BF16) {
+      if (k <= 2) MOE_BDX_K(bf16_t, 2, 2);
+      else if (k <= 4) MOE_BDX_K(bf16_t, 4, 2);
+      else MOE_BDX_K(bf16_t, 8, 1);
+    } else {
+      if (k <= 2) MOE_BDX_K(float, 2, 2);
+      else if (k <= 4) MOE_BDX_K(float, 4, 2);
+      else MOE_BDX_K(float, 8, 1);
+    }
+    return hipGetLastError();
+  }
+#undef MOE_BDX_K
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(backward_dx_kernel<bf16_t>, dim3(tok_grid(T)), dim3(256), 0, s, (const bf16_t*)dxp, p2r, idx, dl,
                        (const bf16_t*)wg, (bf16_t*)dx, T, D, E, k, all_experts);

@@ -34,6 +34,8 @@ CASES = {
                                 bias="normal0.5", seed=62),
     "capacity": W.MoEConfig(name="capacity", T=400, D=128, E=6, top_k=2, F=128, capacity_factor=0.8, seed=63),
     "skew_small": W.get_config("skew", T=1024, D=256, F=192),
+    # k > 8: the general combine, backward combine and dx kernels (the others keep k rows in registers)
+    "k10_general": W.MoEConfig(name="k10_general", T=200, D=128, E=16, top_k=10, F=128, seed=64),
 }
 
 
