@@ -465,55 +465,74 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   }
   const int ldo = (EPI == EPI_BWD && SWI) ? 2 * Nout : Nout;   // out row stride
   const int ldp = SWI ? 2 * Nout : Nout;                         // pre row stride
+  // Through LDS as the plain epilogue, with the float32 accumulators staged (the activation and its
+  // derivative need them unrounded): each wave puts its 32-row blocks (64 columns: 32 of W1 x then 32
+  // of W3 x for the paired tile) in the ring slot the last stage did not read, then each lane takes
+  // 8 consecutive output columns of a row, so every global access is a 16-byte row piece.
+  constexpr int SROWF = 64 + 4;                  // staging row stride (floats; rows stay 16-byte aligned)
+  constexpr int OCW = DUAL ? 32 : 64;            // output columns per wave
+  constexpr int LPR = OCW / 8, RPI = MOE_WAVE / LPR;
+  float* stg = reinterpret_cast<float*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROWF;
+  const int cw = DUAL ? wn * 32 : wn * 64;
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
-    const int r = (2 * i + wm) * 32 + lane % 32;
-    if (i >= act || r >= mrows) continue;
-    bf16_t* orow = out + (size_t)(row0 + r) * ldo + n0;
-    bf16_t* prow = (EPI != EPI_PLAIN) ? pre + (size_t)(row0 + r) * ldp + n0 : nullptr;
+    if (i >= act) continue;
 #pragma unroll
-    for (int j = 0; j < (DUAL ? 1 : 2); ++j)
+    for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = (DUAL ? wn * 32 : wn * 64 + j * 32) + 8 * q + 4 * (lane / 32);
-        if (n0 + c >= Nout) continue;
-        bf16x4 pk;
-        if constexpr (EPI == EPI_BWD) {
-          const bf16x4 a1 = *reinterpret_cast<const bf16x4*>(prow + c);
-          bf16x4 pk3;
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(stg + (lane % 32) * SROWF + jb * 32 + 8 * q + 4 * (lane / 32)) =
+            f32x4{acc[i][jb][4 * q], acc[i][jb][4 * q + 1], acc[i][jb][4 * q + 2], acc[i][jb][4 * q + 3]};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float dh = acc[i][j][4 * q + u], x1 = bf2f(a1[u]);
-            if constexpr (SWI) {
-              const float x3 = bf2f((*reinterpret_cast<const bf16x4*>(prow + Nout + c))[u]);
-              pk[u] = f2bf(dh * x3 * act_silu_grad(x1));
-              pk3[u] = f2bf(dh * act_silu(x1));
-            } else {
-              pk[u] = f2bf(dh * act_gelu_grad(x1));
-            }
-          }
-          *reinterpret_cast<bf16x4*>(orow + c) = pk;
-          if constexpr (SWI) *reinterpret_cast<bf16x4*>(orow + Nout + c) = pk3;
-        } else {
-          bf16x4 p1, p3;
+    for (int rr = 0; rr < 32; rr += RPI) {
+      const int r2 = rr + lane / LPR, c2 = (lane % LPR) * 8;
+      const int r = (2 * i + wm) * 32 + r2, c = n0 + cw + c2;
+      if (r >= mrows || c >= Nout) continue;
+      const float* sr = stg + r2 * SROWF + c2;
+      float v1[8], v3[8];  // W1 x (or dh) and, for the paired tile, W3 x of the 8 columns
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float h = acc[i][j][4 * q + u];
-            if constexpr (EPI == EPI_PRE) {
-              p1[u] = f2bf(h);
-              if constexpr (SWI && DUAL) p3[u] = f2bf(acc[i][1][4 * q + u]);
-            }
-            if constexpr (SWI && DUAL) h = act_silu_fast(h) * acc[i][1][4 * q + u];
-            else if constexpr (ACTFN == MOE_ACT_GELU) h = act_gelu(h);
-            pk[u] = f2bf(h);
-          }
-          *reinterpret_cast<bf16x4*>(orow + c) = pk;
-          if constexpr (EPI == EPI_PRE) {
-            *reinterpret_cast<bf16x4*>(prow + c) = p1;
-            if constexpr (SWI && DUAL) *reinterpret_cast<bf16x4*>(prow + Nout + c) = p3;
-          }
-        }
+      for (int u = 0; u < 8; ++u) {
+        v1[u] = sr[u];
+        if constexpr (DUAL) v3[u] = sr[32 + u];
       }
+      bf16_t* orow = out + (size_t)(row0 + r) * ldo;
+      bf16_t* prow = pre + (size_t)(row0 + r) * ldp;
+      if constexpr (EPI == EPI_BWD) {
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(prow + c);
+        bf16x8 o1, o3;
+        if constexpr (SWI) {
+          const bf16x8 a3 = *reinterpret_cast<const bf16x8*>(prow + Nout + c);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const float x1 = bf2f(a1[u]), x3 = bf2f(a3[u]);
+            o1[u] = f2bf(v1[u] * x3 * act_silu_grad(x1));
+            o3[u] = f2bf(v1[u] * act_silu(x1));
+          }
+          *reinterpret_cast<bf16x8*>(orow + Nout + c) = o3;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) o1[u] = f2bf(v1[u] * act_gelu_grad(bf2f(a1[u])));
+        }
+        *reinterpret_cast<bf16x8*>(orow + c) = o1;
+      } else {  // EPI_PRE
+        bf16x8 o, p1, p3;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          float h = v1[u];
+          p1[u] = f2bf(h);
+          if constexpr (SWI && DUAL) {
+            p3[u] = f2bf(v3[u]);
+            h = act_silu_fast(h) * v3[u];
+          } else if constexpr (ACTFN == MOE_ACT_GELU) {
+            h = act_gelu(h);
+          }
+          o[u] = f2bf(h);
+        }
+        *reinterpret_cast<bf16x8*>(orow + c) = o;
+        *reinterpret_cast<bf16x8*>(prow + c) = p1;
+        if constexpr (SWI && DUAL) *reinterpret_cast<bf16x8*>(prow + Nout + c) = p3;
+      }
+    }
   }
 }
 
