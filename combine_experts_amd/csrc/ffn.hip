@@ -149,7 +149,35 @@ __device__ __forceinline__ int block_scan_g(int v, int* lds, int* total) {
 __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT, int* e_out, int* mt_out,
                              int* nt_out) {
   __shared__ int s_tmp[GW];
-  __shared__ int s_e, s_local;
+  __shared__ int s_e, s_local, s_cnt;
+  if (E <= GTH) {
+    // one scan gives every expert's tile count, its first tile and the total
+    const int e = threadIdx.x;
+    const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const int n = ((cnt + GBM - 1) / GBM) * NT;
+    int L;
+    const int start = block_scan_g(n, s_tmp, &L);
+    const int per = (L + 7) / 8;
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    if (j >= per) return false;
+    const int t = xcd * per + j;
+    if (t >= L) return false;
+    if (e < E && t >= start && t < start + n) {
+      s_e = e;
+      s_local = t - start;
+      s_cnt = cnt;
+    }
+    __syncthreads();
+    const int ee = s_e;
+    const int MT = (s_cnt + GBM - 1) / GBM;
+    const int gsz = G_GN * MT;
+    const int g = s_local / gsz, r = s_local % gsz;
+    const int gn = min(G_GN, NT - g * G_GN);
+    *e_out = ee;
+    *mt_out = r / gn;
+    *nt_out = g * G_GN + r % gn;
+    return true;
+  }
   int L = 0;  // total tiles
   for (int base = 0; base < E; base += GTH) {
     const int e = base + threadIdx.x;
