@@ -147,13 +147,14 @@ __device__ __forceinline__ int block_scan_g(int v, int* lds, int* total) {
 
 // This block's (expert, row tile, column tile), or false when it has none.
 __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT, int* e_out, int* mt_out,
-                             int* nt_out) {
+                             int* nt_out, int* o0_out, int* cnt_out) {
   __shared__ int s_tmp[GW];
-  __shared__ int s_e, s_local, s_cnt;
+  __shared__ int s_e, s_local, s_cnt, s_o0;
   if (E <= GTH) {
     // one scan gives every expert's tile count, its first tile and the total
     const int e = threadIdx.x;
-    const int cnt = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    const int o0 = (e < E) ? offsets[e] : 0;
+    const int cnt = (e < E) ? offsets[e + 1] - o0 : 0;
     const int n = ((cnt + GBM - 1) / GBM) * NT;
     int L;
     const int start = block_scan_g(n, s_tmp, &L);
@@ -166,6 +167,7 @@ __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT,
       s_e = e;
       s_local = t - start;
       s_cnt = cnt;
+      s_o0 = o0;
     }
     __syncthreads();
     const int ee = s_e;
@@ -176,6 +178,8 @@ __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT,
     *e_out = ee;
     *mt_out = r / gn;
     *nt_out = g * G_GN + r % gn;
+    *o0_out = s_o0;
+    *cnt_out = s_cnt;
     return true;
   }
   int L = 0;  // total tiles
@@ -208,13 +212,16 @@ __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT,
   }
   __syncthreads();
   const int e = s_e;
-  const int MT = (offsets[e + 1] - offsets[e] + GBM - 1) / GBM;
+  const int o0 = offsets[e], cnt = offsets[e + 1] - o0;
+  const int MT = (cnt + GBM - 1) / GBM;
   const int gsz = G_GN * MT;
   const int g = s_local / gsz, r = s_local % gsz;
   const int gn = min(G_GN, NT - g * G_GN);
   *e_out = e;
   *mt_out = r / gn;
   *nt_out = g * G_GN + r % gn;
+  *o0_out = o0;
+  *cnt_out = cnt;
   return true;
 }
 
@@ -303,8 +310,12 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
       for (int j = 0; j < 2; ++j) fb[r][j] = s[fi.b[j]];
     }
   };
+  // the first stage's weight slices go first: their addresses need no row lookup, so their latency
+  // overlaps that of the gathered row indices the A loads wait for
 #pragma unroll
-  for (int i = 0; i < G_LPS; ++i) issue(0, 0, i);
+  for (int i = G_NAL; i < G_LPS; ++i) issue(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < G_NAL; ++i) issue(0, 0, i);
   wait_vmcnt<0>();
   __syncthreads();
   frag(0, 0, 0);
@@ -374,10 +385,10 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
   __shared__ bf16x8 lds[2 * G_STAGE];
   const int NT = (Nout + BNO - 1) / BNO;
-  int e, mt, nt;
-  if (!map_tile_xcd(offsets, E, NT, &e, &mt, &nt)) return;
-  const int row0 = offsets[e] + mt * GBM;
-  const int mrows = min(GBM, offsets[e + 1] - row0);
+  int e, mt, nt, o0, cnt;
+  if (!map_tile_xcd(offsets, E, NT, &e, &mt, &nt, &o0, &cnt)) return;
+  const int row0 = o0 + mt * GBM;
+  const int mrows = min(GBM, cnt - mt * GBM);
   const int n0 = nt * BNO;
   const int lane = threadIdx.x % MOE_WAVE;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
