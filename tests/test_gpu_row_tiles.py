@@ -4,7 +4,8 @@ The bf16 grouped GEMM covers an expert's rows with 320-row tiles (the last one p
 counts here hit every case: an empty expert, one row, a 32-row edge, exactly one full tile, one row
 past it, partial second and third tiles, and an expert with more than ten tiles. Up- and down-projection (plain, gathered rows from x, and the K-major weight
 read of the backward data gradient) are compared row by row with the oracle's expert FFN on the same
-rows; the gathered up-projection equals the one on permuted rows bit for bit."""
+rows; the gathered up-projection equals the one on permuted rows bit for bit. A second set has more
+experts than a GEMM block has threads, which takes the tile map's multi-pass scan."""
 import numpy as np
 import pytest
 import torch
@@ -85,3 +86,28 @@ def test_data_gradients_on_every_row_split():
     for name, got, ref in (("da", da, ref_da), ("dx_perm", dx, ref_dx)):
         err = rel_err_rows(f64(got), ref)
         assert err.max() <= TOL_Y[cfg.dtype], f"{name}: max rel err {err.max():.3e} at row {int(err.argmax())}"
+
+
+@needs_gpu
+def test_more_experts_than_block_threads():
+    # 600 experts (the tile map scans the per-expert tile counts in several block-wide passes)
+    print("[row_tiles] 600 experts", flush=True)
+    rng = np.random.default_rng(94)
+    counts = rng.integers(0, 40, size=600)
+    counts[::7] = 0
+    counts[5] = 700  # one expert with three row tiles
+    E, N = len(counts), int(counts.sum())
+    cfg = W.MoEConfig(name="many_experts", T=N, D=64, E=E, top_k=1, F=64, seed=95)
+    inp = W.make_inputs(cfg, "cuda")
+    d = M.dims_from_config(cfg)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device="cuda")
+    x_perm = inp["x"]
+    h = torch.full((N, cfg.F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((N, cfg.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_up(d, x_perm, offsets, inp["w1"], inp["w3"], h)
+    M.moe_expert_ffn_down(d, h, offsets, inp["w2"], y)
+    torch.cuda.synchronize()
+    experts = np.repeat(np.arange(E), counts)
+    ref = O.expert_ffn_rows(x_perm.cpu(), experts, inp["w1"].cpu(), inp["w3"].cpu(), inp["w2"].cpu(), cfg.act)
+    err = rel_err_rows(f64(y), ref)
+    assert err.max() <= TOL_Y[cfg.dtype], f"max rel err {err.max():.3e} at row {int(err.argmax())}"
