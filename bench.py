@@ -209,9 +209,11 @@ def measure_overlap(M, W, torch, cfg, inp, stream, time_calls, n_chunks=2):
 
 def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
     """One training step's backward at the workload shape, stage by stage (HIP events on the stream); the
-    data-gradient GEMMs read the weights as stored (no transposed copies to rebuild after an update)."""
+    data-gradient GEMMs read the weights as stored (no transposed copies to rebuild after an update), and
+    no x_perm is kept: the training up-projection and the transposed x operand of the W1/W3 gradient
+    gather their rows from x."""
     d = M.dims_from_config(cfg)
-    buf = M.MoELayerBuffers(d, device="cuda", logits=True)
+    buf = M.MoELayerBuffers(d, device="cuda", logits=True, x_perm=False)
     bw = M.BackwardBuffers(d, device="cuda")
     g = torch.Generator(device="cuda")
     g.manual_seed(11)
@@ -236,8 +238,8 @@ def measure_backward(M, W, torch, cfg, inp, stream, reps=3):
         ("wgrad_w2", lambda: M.moe_expert_wgrad(d, bw.dyp_t, bw.h_t, bw.koff, d.D, d.F, bw.dw2, stream=stream)),
         ("transpose_da_x", lambda: (M.moe_group_transpose(d, bw.da, nm * d.F, buf.expert_offsets, bw.koff, bw.da_t,
                                                           stream),
-                                    M.moe_group_transpose(d, buf.x_perm, d.D, buf.expert_offsets, bw.koff, bw.xp_t,
-                                                          stream))),
+                                    M.moe_group_transpose_gather(d, x, d.D, buf.expert_offsets, buf.row_to_pair,
+                                                                 bw.koff, bw.xp_t, stream))),
         ("wgrad_w13", lambda: M.moe_expert_wgrad(d, bw.da_t, bw.xp_t, bw.koff, nm * d.F, d.D, bw.dw1, bw.dw3,
                                                  split=d.F, stream=stream)),
     ]

@@ -10,7 +10,7 @@ from ._lib import (  # noqa: F401
     moe_load_balance, moe_dispatch_layout, moe_dispatch_matrix, moe_recv_layout, moe_gather_rows, moe_scatter_rows,
     moe_padded_layout, moe_permute_padded, moe_expert_ffn_padded_up, moe_expert_ffn_padded_down,
     moe_unpermute_combine_add, moe_layer_forward, moe_layer_args, moe_event_create, moe_event_destroy,
-    moe_expert_ffn_up_train, moe_transpose_weights, moe_backward_combine, moe_expert_ffn_down_backward,
+    moe_expert_ffn_up_train, moe_expert_ffn_up_train_gather, moe_group_transpose_gather, moe_transpose_weights, moe_backward_combine, moe_expert_ffn_down_backward,
     moe_expert_ffn_up_backward, moe_expert_ffn_down_backward_w, moe_expert_ffn_up_backward_w, moe_router_backward, moe_backward_dx, moe_wgrad_ld, moe_group_transpose,
     moe_expert_wgrad, MOE_STAGE_ROUTER_BWD, moe_layer_backward, moe_backward_args,
     moe_permute, moe_expert_ffn, moe_expert_ffn_up, moe_expert_ffn_up_gather, moe_expert_ffn_down,

@@ -78,6 +78,7 @@ _SIG = {
                                          _P, _P]),
     "moe_event_create": (ctypes.c_int, [ctypes.POINTER(_P)]),
     "moe_expert_ffn_up_train": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_up_train_gather": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_transpose_weights": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_backward_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_down_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
@@ -90,6 +91,8 @@ _SIG = {
     "moe_wgrad_ld": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(ctypes.c_int64)]),
     "moe_group_transpose": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, ctypes.c_int32, _P, _P, _P, ctypes.c_int64,
                                            _P]),
+    "moe_group_transpose_gather": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, ctypes.c_int32, _P, _P, _P, _P,
+                                                  ctypes.c_int64, _P]),
     "moe_expert_wgrad": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int64, _P, _P, ctypes.c_int32, _P]),
     "moe_event_destroy": (ctypes.c_int, [_P]),
@@ -448,6 +451,17 @@ def moe_expert_ffn_up_train(d: moe_dims, x_perm, expert_offsets, w1, w3, h, pre,
     _check("moe_expert_ffn_up_train", st)
 
 
+def moe_expert_ffn_up_train_gather(d: moe_dims, x, row_to_pair, expert_offsets, w1, w3, h, pre, stream=None) -> None:
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_up_train_gather(
+        ctypes.byref(d), _ptr(x, "x", dt, d.T * d.D), _ptr(row_to_pair, "row_to_pair", torch.int32, P),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w1, "w1", dt, d.E * d.F * d.D), _ptr(w3, "w3", dt, d.E * d.F * d.D, nullable=d.act == MOE_ACT_GELU),
+        _ptr(h, "h", dt, P * d.F), _ptr(pre, "pre", dt, P * d.F * _nm(d)), _stream(stream))
+    _check("moe_expert_ffn_up_train_gather", st)
+
+
 def moe_transpose_weights(d: moe_dims, w1, w3, w2, w13t, w2t, stream=None) -> None:
     dt = _elem_dtype(d)
     n = d.E * d.F * d.D
@@ -549,6 +563,18 @@ def moe_group_transpose(d: moe_dims, src, n_cols: int, expert_offsets, koff, dst
         _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
         _ptr(koff, "koff", torch.int32, d.E + 1), _ptr(dst, "dst", dt, n_cols * moe_wgrad_ld(d)), ld, _stream(stream))
     _check("moe_group_transpose", st)
+
+
+def moe_group_transpose_gather(d: moe_dims, x, n_cols: int, expert_offsets, row_to_pair, koff, dst,
+                               stream=None) -> None:
+    dt = _elem_dtype(d)
+    ld = dst.numel() // max(1, n_cols)
+    st = load_library().moe_group_transpose_gather(
+        ctypes.byref(d), _ptr(x, "x", dt, nullable=d.T == 0), int(n_cols),
+        _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(row_to_pair, "row_to_pair", torch.int32, nullable=d.T == 0),
+        _ptr(koff, "koff", torch.int32, d.E + 1), _ptr(dst, "dst", dt, n_cols * moe_wgrad_ld(d)), ld, _stream(stream))
+    _check("moe_group_transpose_gather", st)
 
 
 def moe_expert_wgrad(d: moe_dims, a_t, b_t, koff, M: int, N: int, out0, out1=None, split=None, stream=None) -> None:

@@ -455,12 +455,14 @@ __global__ void __launch_bounds__(256) group_koff_kernel(const int32_t* __restri
 
 // dst[c][koff[g] + j] = src[off[g] + j][c] for j < count_g, 0 for count_g <= j < padded count;
 // 64-column tiles of the padded axis (each inside one group, as the padded groups are 64-aligned) x
-// 64-row tiles of c, 16-byte global reads and writes. Requires C % VN == 0.
+// 64-row tiles of c, 16-byte global reads and writes. Requires C % VN == 0. With gidx, source row
+// off[g] + j is src row gidx[off[g] + j] / gdiv instead (the permute fused into the transpose).
 template <typename T>
 __global__ void __launch_bounds__(256) group_transpose_kernel(const T* __restrict__ src, int C,
                                                               const int32_t* __restrict__ off,
                                                               const int32_t* __restrict__ koff, int G,
-                                                              T* __restrict__ dst, long long ld) {
+                                                              T* __restrict__ dst, long long ld,
+                                                              const int32_t* __restrict__ gidx, int gdiv) {
   constexpr int VN = 16 / sizeof(T), CPR = 64 / VN;
   __shared__ __attribute__((aligned(16))) T tile[64][64 + VN];
   const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
@@ -479,7 +481,10 @@ __global__ void __launch_bounds__(256) group_transpose_kernel(const T* __restric
     const int jl = q / CPR, cc = q % CPR;
     const int c = c0 + cc * VN;
     u32x4 raw = {0u, 0u, 0u, 0u};
-    if (jl < valid && c < C) raw = *reinterpret_cast<const u32x4*>(src + (size_t)(base + jl) * C + c);
+    if (jl < valid && c < C) {
+      const size_t srow = gidx ? (size_t)(gidx[base + jl] / gdiv) : (size_t)(base + jl);
+      raw = *reinterpret_cast<const u32x4*>(src + srow * C + c);
+    }
     const T* v = reinterpret_cast<const T*>(&raw);
 #pragma unroll
     for (int i = 0; i < VN; ++i) tile[cc * VN + i][jl] = v[i];
@@ -616,15 +621,15 @@ hipError_t launch_group_koff(const int32_t* off, int G, int32_t* koff, hipStream
 }
 
 hipError_t launch_group_transpose(const void* src, int C, const int32_t* off, const int32_t* koff, int G,
-                                  long long ld, void* dst, int dtype, hipStream_t s) {
+                                  long long ld, void* dst, int dtype, hipStream_t s, const int32_t* gidx, int gdiv) {
   if (ld == 0 || C == 0) return hipSuccess;
   const dim3 grid((unsigned)((ld + 63) / 64), (C + 63) / 64);
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(group_transpose_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)src, C, off, koff, G,
-                       (bf16_t*)dst, ld);
+                       (bf16_t*)dst, ld, gidx, gdiv);
   else
     hipLaunchKernelGGL(group_transpose_kernel<float>, grid, dim3(256), 0, s, (const float*)src, C, off, koff, G,
-                       (float*)dst, ld);
+                       (float*)dst, ld, gidx, gdiv);
   return hipGetLastError();
 }
 

@@ -33,7 +33,6 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
   if (d == nullptr || a == nullptr) return MOE_ERR_INVALID_ARG;
   if (n_chunks < 1 || d->T % n_chunks != 0) return MOE_ERR_INVALID_ARG;
   if (side_stream != nullptr && events == nullptr) return MOE_ERR_INVALID_ARG;
-  if (a->x_perm == nullptr && a->pre != nullptr) return MOE_ERR_INVALID_ARG;  // training keeps x_perm
   if (a->shared_w1 != nullptr && (a->shared_F <= 0 || !a->shared_w2 || !a->shared_h || !a->shared_y ||
                                   !a->shared_offsets || (d->act == MOE_ACT_SWIGLU && !a->shared_w3)))
     return MOE_ERR_INVALID_ARG;
@@ -88,7 +87,9 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
     }
     if (a->pre != nullptr) {
       void* pc = static_cast<char*>(a->pre) + p0 * (int64_t)d->F * (d->act == MOE_ACT_SWIGLU ? 2 : 1) * eb;
-      if ((st = moe_expert_ffn_up_train(&c, xp, eoff, a->w1, a->w3, hc, pc, fs)) != MOE_OK) return st;
+      st = xp ? moe_expert_ffn_up_train(&c, xp, eoff, a->w1, a->w3, hc, pc, fs)
+              : moe_expert_ffn_up_train_gather(&c, xc, a->row_to_pair + p0, eoff, a->w1, a->w3, hc, pc, fs);
+      if (st != MOE_OK) return st;
     } else if (xp) {
       if ((st = moe_expert_ffn_up(&c, xp, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) return st;
     } else if ((st = moe_expert_ffn_up_gather(&c, xc, a->row_to_pair + p0, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) {
@@ -146,8 +147,11 @@ int moe_layer_backward(const moe_dims* d, const moe_backward_args* a, hipStream_
     return st;
   if ((st = moe_group_transpose(d, a->da, nm * d->F, a->expert_offsets, a->koff, a->da_t, a->ld, stream)) != MOE_OK)
     return st;
-  if ((st = moe_group_transpose(d, a->x_perm, d->D, a->expert_offsets, a->koff, a->x_perm_t, a->ld, stream)) != MOE_OK)
-    return st;
+  // x_perm^T, or, without a saved x_perm, the same rows gathered from x on the way into the transpose
+  st = a->x_perm ? moe_group_transpose(d, a->x_perm, d->D, a->expert_offsets, a->koff, a->x_perm_t, a->ld, stream)
+                 : moe_group_transpose_gather(d, a->x, d->D, a->expert_offsets, a->row_to_pair, a->koff, a->x_perm_t,
+                                              a->ld, stream);
+  if (st != MOE_OK) return st;
   return moe_expert_wgrad(d, a->da_t, a->x_perm_t, a->koff, nm * d->F, d->D, a->ld, a->dw1, a->dw3, d->F, stream);
 }
 

@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 106;
+constexpr int kAbiVersion = 107;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -373,6 +373,23 @@ int moe_expert_ffn_up_train(const moe_dims* d, const void* x_perm, const int32_t
   return hip_status(moe::launch_ffn_bf16(a, stream));
 }
 
+int moe_expert_ffn_up_train_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
+                                   const int32_t* expert_offsets, const void* w1, const void* w3, void* h, void* pre,
+                                   hipStream_t stream) {
+  int st = ffn_bwd_common(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!x || !row_to_pair || !expert_offsets || !w1 || !h || !pre || (d->act == MOE_ACT_SWIGLU && !w3))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(h) || !aligned16(pre) || (w3 && !aligned16(w3)))
+    return MOE_ERR_INVALID_ARG;
+  moe::FfnArgs a{x, expert_offsets, w1, d->act == MOE_ACT_SWIGLU ? w3 : nullptr, h,
+                 d->T * d->top_k, d->E, d->D, d->F, d->act, 1, pre};
+  a.gather = row_to_pair;
+  a.gather_div = d->top_k;
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
 int moe_transpose_weights(const moe_dims* d, const void* w1, const void* w3, const void* w2, void* w13t, void* w2t,
                           hipStream_t stream) {
   int st = check_dims(d);
@@ -507,6 +524,23 @@ int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, cons
   if (!row_vec_ok(d, n_cols)) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
   hipError_t e = moe::launch_group_koff(expert_offsets, d->E, koff, stream);
   if (e == hipSuccess) e = moe::launch_group_transpose(src, n_cols, expert_offsets, koff, d->E, ld, dst, d->dtype, stream);
+  return hip_status(e);
+}
+
+int moe_group_transpose_gather(const moe_dims* d, const void* x, int32_t n_cols, const int32_t* expert_offsets,
+                               const int32_t* row_to_pair, int32_t* koff, void* dst, int64_t ld, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  int64_t need = 0;
+  moe_wgrad_ld(d, &need);
+  if (n_cols < 0 || ld < need) return MOE_ERR_INVALID_ARG;
+  if (!expert_offsets || !koff || (ld > 0 && n_cols > 0 && (!dst || (d->T > 0 && (!x || !row_to_pair)))))
+    return MOE_ERR_INVALID_ARG;
+  if (!row_vec_ok(d, n_cols)) return MOE_ERR_UNSUPPORTED;  // 16-byte row chunks
+  hipError_t e = moe::launch_group_koff(expert_offsets, d->E, koff, stream);
+  if (e == hipSuccess)
+    e = moe::launch_group_transpose(x, n_cols, expert_offsets, koff, d->E, ld, dst, d->dtype, stream, row_to_pair,
+                                    d->top_k);
   return hip_status(e);
 }
 

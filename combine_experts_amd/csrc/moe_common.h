@@ -100,7 +100,8 @@ hipError_t launch_transpose(const void* src, int B, int R, int C, long long src_
                             long long dst_batch, int col_off, int dtype, hipStream_t s);
 hipError_t launch_group_koff(const int32_t* off, int G, int32_t* koff, hipStream_t s);
 hipError_t launch_group_transpose(const void* src, int C, const int32_t* off, const int32_t* koff, int G,
-                                  long long ld, void* dst, int dtype, hipStream_t s);
+                                  long long ld, void* dst, int dtype, hipStream_t s, const int32_t* gidx = nullptr,
+                                  int gdiv = 1);
 
 struct FfnArgs {
   const void* a;              // x_perm (up) or h (down): [N_max, K]

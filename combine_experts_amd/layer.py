@@ -16,7 +16,8 @@ from . import _lib as L
 class MoELayerBuffers:
     def __init__(self, d: L.moe_dims, device="cuda", logits: bool = False, x_perm: bool = True):
         """x_perm=False: no permuted copy of x; the forward's up-projection gathers its rows from x
-        (``moe_expert_ffn_up_gather``). Training (``forward_train``) needs x_perm."""
+        (``moe_expert_ffn_up_gather``; in training ``moe_expert_ffn_up_train_gather``, and the backward
+        gathers the same rows into its transposed operand)."""
         self.d = d
         dt = torch.bfloat16 if d.dtype == L.MOE_BF16 else torch.float32
         P = d.T * d.top_k
@@ -192,8 +193,8 @@ class BackwardBuffers:
 
 def forward_train(buf: MoELayerBuffers, bw: "BackwardBuffers", x, w_gate, bias, w1, w3, w2, stream=None):
     """The forward with what the backward needs saved: logits (buf must hold them) and pre-activations."""
-    if buf.logits is None or buf.x_perm is None:
-        raise ValueError("forward_train needs MoELayerBuffers(..., logits=True, x_perm=True)")
+    if buf.logits is None:
+        raise ValueError("forward_train needs MoELayerBuffers(..., logits=True)")
     L.moe_layer_forward(buf.d, _layer_args(buf, x, w_gate, bias, w1, w3, w2, pre=bw.pre), 1, stream)
     return buf.y
 

@@ -299,7 +299,8 @@ typedef struct moe_layer_args {
   int32_t* pair_to_row;      /* [T*top_k] */
   int32_t* row_to_pair;      /* [T*top_k] */
   void* x_perm;              /* [T*top_k, D], or NULL: the up-projection gathers its rows from x
-                                (moe_expert_ffn_up_gather); required when pre is set */
+                                (moe_expert_ffn_up_gather, or moe_expert_ffn_up_train_gather when pre
+                                is set) */
   void* h;                   /* [T*top_k, F] */
   void* y_perm;              /* [T*top_k, D] */
   int32_t* expert_counts;    /* [n_chunks, E] */
@@ -353,6 +354,12 @@ int moe_event_destroy(hipEvent_t event);
 int moe_expert_ffn_up_train(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
                             const void* w1, const void* w3, void* h, void* pre, hipStream_t stream);
 
+/* moe_expert_ffn_up_train with its rows gathered from x (x_perm[r] = x[row_to_pair[r] / top_k], as
+ * moe_expert_ffn_up_gather): the same h and pre, bit for bit, with no x_perm. */
+int moe_expert_ffn_up_train_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
+                                   const int32_t* expert_offsets, const void* w1, const void* w3, void* h,
+                                   void* pre, hipStream_t stream);
+
 /* The weights as the data-gradient GEMMs read them: w2t [E, F, D] = W2^T; w13t [E, D, 2F] =
  * [W1^T | W3^T] (SwiGLU) or [E, D, F] = W1^T (GELU). Once per weight update. */
 int moe_transpose_weights(const moe_dims* d, const void* w1, const void* w3, const void* w2, void* w13t,
@@ -405,6 +412,12 @@ int moe_wgrad_ld(const moe_dims* d, int64_t* ld);
 int moe_group_transpose(const moe_dims* d, const void* src, int32_t n_cols, const int32_t* expert_offsets,
                         int32_t* koff, void* dst, int64_t ld, hipStream_t stream);
 
+/* moe_group_transpose of x_perm without x_perm: row r of the source is x[row_to_pair[r] / top_k]
+ * (x [T, n_cols]), the permute done by the transpose's loads; the same dst bit for bit. */
+int moe_group_transpose_gather(const moe_dims* d, const void* x, int32_t n_cols, const int32_t* expert_offsets,
+                               const int32_t* row_to_pair, int32_t* koff, void* dst, int64_t ld,
+                               hipStream_t stream);
+
 /* Per expert e: out_e[m, n] = sum over columns [koff[e], koff[e+1]) of a_t[m, col] * b_t[n, col]
  * (a_t [M, ld], b_t [N, ld] bf16, as moe_group_transpose writes them); rows m < split go to
  * out0 [E, split, N], the rest to out1 [E, M - split, N] (float32). dW2 = wgrad(dy_perm^T, h^T,
@@ -422,7 +435,8 @@ typedef struct moe_backward_args {
   const void* x; const void* w_gate; const void* w1; const void* w3; const void* w2;
   const float* logits; const int32_t* topk_idx; const float* topk_gate;
   const int32_t* expert_offsets; const int32_t* pair_to_row; const int32_t* row_to_pair;
-  const void* x_perm; const void* h; const void* pre; const void* y_perm;   /* saved forward tensors */
+  const void* x_perm; const void* h; const void* pre; const void* y_perm;   /* saved forward tensors;
+                                                   x_perm may be NULL: its rows are gathered from x */
   const void* dy;                                                          /* [T, D] upstream gradient */
   void* w13t; void* w2t; int32_t refresh_weights;
   void* dy_perm; float* dgate; void* da; void* dx_perm; float* dl;         /* backward activations */

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 106
+    assert M.moe_abi_version() == 107
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
