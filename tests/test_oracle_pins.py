@@ -447,3 +447,84 @@ def test_itertools_sanity():
     row = [0.3, -1.0, 2.0, 2.0, 0.0]
     best = max(itertools.combinations(range(5), 3), key=lambda c: (sum(row[i] for i in c), [-i for i in c]))
     assert sorted(_topk_by_rank_counting(row, 3)) == sorted(best)
+
+
+# ------------------------------------------------------------------------------------------------
+# Metamorphic checks on the whole layer: relabelled experts, permuted tokens, zero and identical
+# experts. Each follows from the layer equation y = sum over the chosen experts of gate * expert(x)
+# without reference to how the oracle computes it.
+# ------------------------------------------------------------------------------------------------
+
+def _small_layer(seed, T=24, D=8, E=6, k=2, F=5, capacity_factor=0.0, gate=None, act=None):
+    rng = np.random.default_rng(seed)
+    inputs = {"x": rng.standard_normal((T, D)), "w_gate": rng.standard_normal((E, D)),
+              "bias": rng.standard_normal(E) * 0.3,
+              "w1": rng.standard_normal((E, F, D)), "w3": rng.standard_normal((E, F, D)),
+              "w2": rng.standard_normal((E, D, F))}
+    cfg = type("Cfg", (), dict(T=T, D=D, E=E, top_k=k, F=F, n_groups=0, topk_groups=0,
+                                gate=O.GATE_SOFTMAX_TOPK if gate is None else gate,
+                                capacity_factor=capacity_factor, ep_size=1,
+                                act=O.ACT_SWIGLU if act is None else act))
+    return inputs, cfg
+
+
+@pytest.mark.parametrize("capacity_factor", [0.0, 0.75])
+@pytest.mark.parametrize("gate", [O.GATE_SOFTMAX_TOPK, O.GATE_SIGMOID_TOPK])
+def test_relabelled_experts_give_the_same_layer(capacity_factor, gate):
+    # expert e renamed pi[e] (its router row, bias and weights move with it): every token picks the
+    # same experts under their new names, in the same slots, and y does not change; the keep rule
+    # ranks an expert's pairs by pair id, so drops follow the expert too
+    inputs, cfg = _small_layer(20, capacity_factor=capacity_factor, gate=gate)
+    pi = np.array([3, 0, 5, 1, 4, 2])
+    moved = dict(inputs)
+    for key in ("w_gate", "bias", "w1", "w3", "w2"):
+        a = np.empty_like(inputs[key])
+        a[pi] = inputs[key]
+        moved[key] = a
+    ref, got = O.layer_forward(inputs, cfg), O.layer_forward(moved, cfg)
+    np.testing.assert_array_equal(got["topk_idx"], pi[ref["topk_idx"]])
+    np.testing.assert_array_equal(got["topk_gate"], ref["topk_gate"])
+    np.testing.assert_array_equal(got["expert_counts"][pi], ref["expert_counts"])
+    np.testing.assert_array_equal(got["pair_to_row"] >= 0, ref["pair_to_row"] >= 0)
+    np.testing.assert_allclose(got["y"], ref["y"], rtol=1e-12, atol=1e-12)
+
+
+def test_permuted_tokens_permute_the_output():
+    # dropless: a token's output depends on that token alone
+    inputs, cfg = _small_layer(21)
+    sigma = np.random.default_rng(22).permutation(cfg.T)
+    moved = dict(inputs, x=inputs["x"][sigma])
+    ref, got = O.layer_forward(inputs, cfg), O.layer_forward(moved, cfg)
+    np.testing.assert_array_equal(got["topk_idx"], ref["topk_idx"][sigma])
+    np.testing.assert_allclose(got["y"], ref["y"][sigma], rtol=1e-12, atol=1e-12)
+
+
+def test_zero_down_projection_gives_zero_output():
+    inputs, cfg = _small_layer(23)
+    inputs["w2"] = np.zeros_like(inputs["w2"])
+    out = O.layer_forward(inputs, cfg)
+    assert np.all(out["y"] == 0.0)
+    assert np.all(out["y_perm"] == 0.0) and out["n_kept"] == cfg.T * cfg.top_k
+
+
+@pytest.mark.parametrize("act", [O.ACT_SWIGLU, O.ACT_GELU])
+def test_identical_experts_make_a_dense_ffn(act):
+    # every expert the same FFN and the gates of a token summing to 1: the routed sum is that FFN of
+    # the token, whatever the router picked (closed form computed here with plain loops)
+    inputs, cfg = _small_layer(24, T=7, D=4, E=5, k=3, F=3, act=act)
+    for key in ("w1", "w3", "w2"):
+        inputs[key] = np.repeat(inputs[key][:1], cfg.E, axis=0)
+    if act == O.ACT_GELU:
+        inputs["w3"] = None
+    out = O.layer_forward(inputs, cfg)
+    x, w1, w2 = inputs["x"], inputs["w1"][0], inputs["w2"][0]
+    for t in range(cfg.T):
+        a = [sum(w1[f][d] * x[t][d] for d in range(cfg.D)) for f in range(cfg.F)]
+        if act == O.ACT_SWIGLU:
+            w3 = inputs["w3"][0]
+            b = [sum(w3[f][d] * x[t][d] for d in range(cfg.D)) for f in range(cfg.F)]
+            h = [a[f] / (1.0 + math.exp(-a[f])) * b[f] for f in range(cfg.F)]
+        else:
+            h = [0.5 * a[f] * (1.0 + math.erf(a[f] / math.sqrt(2.0))) for f in range(cfg.F)]
+        want = [sum(w2[d][f] * h[f] for f in range(cfg.F)) for d in range(cfg.D)]
+        np.testing.assert_allclose(out["y"][t], want, rtol=1e-11, atol=1e-12)
