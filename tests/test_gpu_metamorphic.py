@@ -11,7 +11,9 @@ where the row sits in a tile, so the GPU must reproduce these properties bit for
 - a zero down-projection gives y = 0;
 - identical experts with gates summing to 1 give every token the same FFN output in each of its k
   rows, and y equal to that row (the float32 gate sum is within a few 2^-24 of 1, far inside the
-  half-spacing of bfloat16, so the single rounding returns it)."""
+  half-spacing of bfloat16, so the single rounding returns it);
+- in the backward, renaming the experts leaves dx unchanged and moves every per-expert gradient
+  (dW_g and bias rows, dW1, dW3, dW2) with its expert."""
 import numpy as np
 import pytest
 import torch
@@ -113,3 +115,41 @@ def test_identical_experts(act):
     yp = r["y_perm"][rows]                                  # [T, k, D]: a token's k expert rows
     assert torch.equal(yp, yp[:, :1].expand_as(yp))         # the same bits in every slot
     assert torch.equal(r["y"], yp[:, 0])
+
+
+def _train_step(cfg, inp, dy):
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device="cuda", logits=True, x_perm=False)
+    bw = M.BackwardBuffers(d, device="cuda")
+    M.forward_train(buf, bw, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    M.backward(buf, bw, inp["x"], inp["w_gate"], dy, transpose_weights=(inp["w1"], inp["w3"], inp["w2"]))
+    torch.cuda.synchronize()
+    out = {n: getattr(bw, n).clone() for n in ("dx", "dw_gate", "dbias", "dw1", "dw2")}
+    out["dw3"] = None if bw.dw3 is None else bw.dw3.clone()
+    return out
+
+
+@needs_gpu
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_renamed_experts_backward(case):
+    # the backward sums an expert's rows in pair-id order and a token's slots in slot order, neither
+    # of which depends on the experts' numbers: dx is unchanged and every per-expert gradient moves
+    # with its expert, bit for bit
+    name, kw, kind = case
+    print(f"[metamorphic] renamed experts, backward {name}", flush=True)
+    cfg = W.MoEConfig(name=name, seed=306, **kw)
+    inp = W.make_inputs(cfg, "cuda")
+    if inp["bias"] is None:
+        inp["bias"] = (torch.randn(cfg.E, generator=torch.Generator().manual_seed(307)) * 0.1).cuda()
+    pi = _renaming(cfg, kind)
+    pi_t = torch.as_tensor(pi, dtype=torch.long, device="cuda")
+    moved = dict(inp)
+    for key in ("w_gate", "bias", "w1", "w3", "w2"):
+        if inp[key] is not None:
+            moved[key] = torch.empty_like(inp[key]).index_copy_(0, pi_t, inp[key])
+    dy = torch.randn((cfg.T, cfg.D), generator=torch.Generator().manual_seed(308)).to(torch.bfloat16).cuda()
+    a, b = _train_step(cfg, inp, dy), _train_step(cfg, moved, dy)
+    assert torch.equal(b["dx"], a["dx"])
+    for n in ("dw_gate", "dbias", "dw1", "dw3", "dw2"):
+        if a[n] is not None:
+            assert torch.equal(b[n][pi_t], a[n]), n
