@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
 // Weight gradients: out_g = A_g^T-free form out_g[m, n] = sum_{k in group g} aT[m, k] * bT[n, k], with
 // both operands stored transposed ([M, ld] and [N, ld], the reduction index contiguous) and group g
 // owning columns [koff[g], koff[g+1]) of both, zero-padded to a multiple of 64. The k-loop is the
-// forward's; tiles are 256 x 256 of (m, n); float32 output, rows m < split to out0[g] ([split, N])
+// forward's; tiles are 320 x 256 of (m, n); float32 output, rows m < split to out0[g] ([split, N])
 // and the rest to out1[g] ([M - split, N]).
 // ---------------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__ aT, const bf16_t* __restrict__ bT,
