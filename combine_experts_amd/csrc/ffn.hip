@@ -97,8 +97,8 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // the 8-byte pieces directly).
 //
 // K runs in 64-deep stages through a 2-slot LDS ring (72 KB per slot). Loads go straight from
-// global memory into LDS (16 bytes per lane, no register staging); a whole stage is issued at once,
-// one stage ahead, at the start of the stage before it. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
+// global memory into LDS (buffer loads with the LDS flag, 16 bytes per lane, no register staging);
+// a whole stage is issued at once, one stage ahead, at the start of the stage before it. Inside a slot each 64-element row of a tile is 8 16-byte chunks stored at chunk
 // ch ^ ((row >> 1) & 7), so the 32 rows one fragment read touches fall on distinct banks.
 //
 // Tile order: a block's tile comes from its index through an XCD-aware map (workgroups are handed
@@ -239,16 +239,30 @@ constexpr int G_NAL = G_ACH / GTH;  // A loads per stage and lane
 // 16-byte chunk c of row k stored at chunk c ^ 4*(k & 3). Rows k < ksplit come from b0 (per expert
 // [ksplit][nout]), the rest from b1 (per expert [K - ksplit][nout]).
 struct BtSrc {
-  const bf16_t* b0;
-  const bf16_t* b1;
   int ksplit, nout;
-  int ofs[G_LPS - G_NAL];  // this lane's element offset (row * nout + column) inside a stage, per B load
-  int tro[2][2];           // byte offsets of the transposed fragment reads (k half h, block j) in the B region
-  __device__ __forceinline__ const bf16_t* stage(int kt) const {
-    const int k0 = kt * GBK;
-    return k0 < ksplit ? b0 + (size_t)k0 * nout : b1 + (size_t)(k0 - ksplit) * nout;
-  }
+  int tro[2][2];  // byte offsets of the transposed fragment reads (k half h, block j) in the B region
 };
+
+// Where a lane's direct loads read: buffer resources for the A rows and the two B sources (the same
+// resource twice for a single B matrix; W1 and W3 for the paired tile; the K-major slices below and
+// above ksplit for BT) and one 32-bit byte offset per load; the stage's K offset goes in the scalar
+// offset. Buffer loads rather than global ones: the compiler then tracks the fragment reads' LDS
+// counter exactly and each MFMA waits only for its own operands (a global load into LDS makes it
+// wait for every LDS read in flight).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+struct DmaSrc {
+  rsrc_t a, b0, b1;
+  uint32_t off[G_LPS];
+};
+
+// raw buffer resource over 4 GiB from base (no stride, no range clamp; word 3 is the gfx9 default)
+__device__ __forceinline__ rsrc_t dma_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, bf16x8* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, soff, 0, 0);
+}
 
 // ds_read_b64_tr_b16: within each 16-lane group, output lane i gets element e from the group's lane
 // 4e + i/4, its element i % 4 (measured on the hardware). With lane 4e + q of the group reading row
@@ -281,20 +295,37 @@ __device__ __forceinline__ FragIdx frag_idx(int lane, int wm, int wn) {
 }
 
 template <int ACT, bool BT>  // ACT: active 32-row blocks of this wave; BT: B stored K-major
-__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const bf16_t* const (&src)[G_LPS],
+__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const DmaSrc& ds,
                                            const FragIdx& fi, const BtSrc& bt, int wave, int nk, int mrows) {
-  // load i fills tile rows [i*64, i*64+64) of A (i < G_NAL) or a part of B; A loads wholly past the
-  // tile's rows are skipped (those rows feed only accumulators that are never stored)
+  // load i fills tile rows [i*64, i*64+64) of A (i < G_NAL) or a part of B (the first half of the B
+  // loads from b0, the rest from b1); A loads wholly past the tile's rows are skipped (those rows
+  // feed only accumulators that are never stored)
   auto issue = [&](int kt, int buf, int i) {
     if (i < G_NAL && i * (GTH / GKCH) >= mrows) return;
-    const bf16_t* p = (BT && i >= G_NAL) ? bt.stage(kt) + bt.ofs[i - G_NAL] : src[i] + kt * GBK;
-    __builtin_amdgcn_global_load_lds((const void*)p,
-                                     (__attribute__((address_space(3))) void*)(lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE),
-                                     16, 0, 0);
+    bf16x8* dst = lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE;
+    if (i < G_NAL) {
+      dma16(ds.a, ds.off[i], kt * GBK * 2, dst);
+    } else if constexpr (BT) {
+      const int k0 = kt * GBK;
+      const bool lo = k0 < bt.ksplit;
+      dma16(lo ? ds.b0 : ds.b1, ds.off[i], (uint32_t)((lo ? k0 : k0 - bt.ksplit) * bt.nout * 2), dst);
+    } else {
+      dma16(i < G_NAL + (G_LPS - G_NAL) / 2 ? ds.b0 : ds.b1, ds.off[i], kt * GBK * 2, dst);
+    }
   };
   bf16x8 fa[2][GMB], fb[2][2];
   auto frag = [&](int buf, int ks, int r) {
     const bf16x8* s = lds + buf * G_STAGE + fi.lane[ks];
+    if constexpr (!BT) {
+      // in the order the next k-step's MFMAs take them (B0 A0, B1, then A1 ...), so that each MFMA
+      // waits only for its own two fragments
+      fb[r][0] = s[fi.b[0]];
+      fa[r][0] = s[fi.a];
+      fb[r][1] = s[fi.b[1]];
+#pragma unroll
+      for (int i = 1; i < ACT; ++i) fa[r][i] = s[fi.a + i * 2 * 32 * GKCH];
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < ACT; ++i) fa[r][i] = s[fi.a + i * 2 * 32 * GKCH];
     if constexpr (BT) {
@@ -305,9 +336,6 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
         const bf16x4 lo = tr_read(sb + bt.tro[0][j]), hi = tr_read(sb + bt.tro[1][j]);
         fb[r][j] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[r][j] = s[fi.b[j]];
     }
   };
   // the first stage's weight slices go first: their addresses need no row lookup, so their latency
@@ -325,14 +353,22 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
 #pragma unroll
     for (int ks = 0; ks < G_KS; ++ks) {
       const int c = ks & 1, n = c ^ 1;
-      // all of stage kt+1 goes to the other slot at once, at the start of stage kt (the slot is free
-      // since the barrier that ended iteration kt-1): the loads get a whole stage to land
-      if (refill && ks == 0) {
+      // all of stage kt+1 goes to the other slot at once (free since the barrier that ended iteration
+      // kt-1), at the start of stage kt: the loads get a whole stage to land. The transposed reads of
+      // the BT form count, for the compiler, as possibly reading what those loads write, so there the
+      // loads go out after the stage's last fragment read instead (else each stage would wait for
+      // them right after issuing them)
+      constexpr int ISSUE_KS = BT ? G_KS - 2 : 0;
+      if (!BT && refill && ks == ISSUE_KS) {
 #pragma unroll
         for (int i = 0; i < G_LPS; ++i) issue(kt + 1, buf ^ 1, i);
       }
       if (ks < G_KS - 1) {
         frag(buf, ks + 1, n);
+        if (BT && refill && ks == ISSUE_KS) {
+#pragma unroll
+          for (int i = 0; i < G_LPS; ++i) issue(kt + 1, buf ^ 1, i);
+        }
       } else if (refill) {
         wait_vmcnt<0>();  // this wave's part of stage kt+1 has landed ...
         __syncthreads();  // ... and everyone's; everyone is also done reading slot buf
@@ -393,46 +429,43 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int lane = threadIdx.x % MOE_WAVE;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
   const int wm = wave / 4, wn = wave % 4;
-  const bf16_t* Ab = A + (size_t)row0 * K;
-  const bf16_t* Bw0 = B0 + ((size_t)e * Nout + n0) * K;
-  const bf16_t* Bw1 = DUAL ? B1 + ((size_t)e * Nout + n0) * K : nullptr;
-
-  // source of each of this lane's direct loads: load i fills LDS slots [i*GTH + wave*64, +64)
-  const bf16_t* src[G_LPS];
+  // this lane's direct loads: load i fills LDS slots [i*GTH + wave*64, +64). A rows come from the
+  // row tile's base, or from x itself (gathered rows: byte offsets from x, which the host keeps under
+  // 4 GiB); the weights from the tile's first weight row
+  DmaSrc ds;
+  ds.a = dma_rsrc(gather ? A : A + (size_t)row0 * K);
 #pragma unroll
-  for (int i = 0; i < G_LPS; ++i) {
+  for (int i = 0; i < G_NAL; ++i) {
     const int slot = i * GTH + wave * MOE_WAVE + lane;
-    if (i * GTH < G_ACH) {
-      const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
-      const int r = row < mrows ? row : 0;
-      src[i] = (gather ? A + (size_t)(gather[row0 + r] / gdiv) * K : Ab + (size_t)r * K) + ch * 8;
-    } else if constexpr (!BT) {
-      const int bs = slot - G_ACH;
-      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
-      const bf16_t* p;
-      if constexpr (DUAL) {
-        const int f = row % (GBR / 2);
-        p = (n0 + f < Nout) ? ((row < GBR / 2 ? Bw0 : Bw1) + (size_t)f * K) : Bw0;
-      } else {
-        p = (n0 + row < Nout) ? Bw0 + (size_t)row * K : Bw0;
-      }
-      src[i] = p + ch * 8;
-    } else {
-      src[i] = nullptr;  // the K-major B loads go through bt
-    }
+    const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
+    const int r = row < mrows ? row : 0;
+    const uint32_t arow = gather ? (uint32_t)(gather[row0 + r] / gdiv) : (uint32_t)r;
+    ds.off[i] = arow * (uint32_t)K * 2u + ch * 16;
   }
   const FragIdx fi = frag_idx<DUAL>(lane, wm, wn);
   BtSrc bt{};
-  if constexpr (BT) {
-    bt.b0 = B0 + (size_t)e * ksplit * Nout + n0;
-    bt.b1 = B1 ? B1 + (size_t)e * (K - ksplit) * Nout + n0 : nullptr;
+  if constexpr (!BT) {
+    ds.b0 = dma_rsrc(B0 + ((size_t)e * Nout + n0) * K);
+    ds.b1 = DUAL ? dma_rsrc(B1 + ((size_t)e * Nout + n0) * K) : ds.b0;
+#pragma unroll
+    for (int i = G_NAL; i < G_LPS; ++i) {
+      const int bs = i * GTH + wave * MOE_WAVE + lane - G_ACH;
+      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
+      // the paired tile's second half (W3 rows) sits in the second half of the B loads; rows past
+      // Nout re-read the slice's first row (never stored)
+      const int f = DUAL ? row % (GBR / 2) : row;
+      ds.off[i] = (n0 + f < Nout ? (uint32_t)f * (uint32_t)K * 2u : 0u) + ch * 16;
+    }
+  } else {
+    ds.b0 = dma_rsrc(B0 + (size_t)e * ksplit * Nout + n0);
+    ds.b1 = B1 ? dma_rsrc(B1 + (size_t)e * (K - ksplit) * Nout + n0) : ds.b0;
     bt.ksplit = ksplit;
     bt.nout = Nout;
 #pragma unroll
     for (int i = G_NAL; i < G_LPS; ++i) {
       const int bs = i * GTH + wave * MOE_WAVE + lane - G_ACH;  // chunk of the B region this lane fills
       const int k = bs / (GBR / 8), c = (bs % (GBR / 8)) ^ ((k & 3) << 2);
-      bt.ofs[i - G_NAL] = k * Nout + (n0 + c * 8 < Nout ? c * 8 : 0);  // columns past Nout: never stored
+      ds.off[i] = (uint32_t)(k * Nout + (n0 + c * 8 < Nout ? c * 8 : 0)) * 2u;  // columns past Nout: never stored
     }
     const int g = lane / 16, e4 = (lane % 16) / 4, q = lane % 4;
 #pragma unroll
@@ -456,11 +489,11 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
-    case 5: gemm_kloop<5, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
-    case 4: gemm_kloop<4, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
-    case 3: gemm_kloop<3, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
-    case 2: gemm_kloop<2, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
-    default: gemm_kloop<1, BT>(acc, lds, src, fi, bt, wave, nk, mrows); break;
+    case 5: gemm_kloop<5, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
+    case 4: gemm_kloop<4, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
+    case 3: gemm_kloop<3, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
+    case 2: gemm_kloop<2, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
+    default: gemm_kloop<1, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
   constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
@@ -599,17 +632,21 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
   const int lane = threadIdx.x % MOE_WAVE;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / MOE_WAVE);
   const int wm = wave / 4, wn = wave % 4;
-  const bf16_t* src[G_LPS];
+  // direct loads from the tile's first operand rows at the group's first reduction column
+  DmaSrc ds;
+  ds.a = dma_rsrc(aT + (size_t)m0 * ld + k0);
+  ds.b0 = dma_rsrc(bT + (size_t)n0 * ld + k0);
+  ds.b1 = ds.b0;
 #pragma unroll
   for (int i = 0; i < G_LPS; ++i) {
     const int slot = i * GTH + wave * MOE_WAVE + lane;
     if (i * GTH < G_ACH) {
       const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
-      src[i] = aT + (size_t)(m0 + (row < mrows ? row : 0)) * ld + k0 + ch * 8;
+      ds.off[i] = (uint32_t)((row < mrows ? row : 0) * ld) * 2u + ch * 16;
     } else {
       const int bs = slot - G_ACH;
       const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
-      src[i] = bT + (size_t)(n0 + row < N ? n0 + row : n0) * ld + k0 + ch * 8;
+      ds.off[i] = (uint32_t)((n0 + row < N ? row : 0) * ld) * 2u + ch * 16;
     }
   }
   const FragIdx fi = frag_idx<false>(lane, wm, wn);
@@ -620,7 +657,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) gemm_kloop<GMB, false>(acc, lds, src, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
+  if (nk > 0) gemm_kloop<GMB, false>(acc, lds, ds, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
   // the tile goes out through LDS: each wave stages its 32-row blocks (32 x 64 floats) in the ring slot
   // the last stage did not read and stores 256-byte row pieces, 16 lanes per row, instead of 16-byte
   // pieces of 32 rows per instruction
@@ -726,6 +763,12 @@ dim3 ffn_grid(const FfnArgs& a, int tbn) {
 
 hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   if (a.n_rows_max == 0) return hipSuccess;
+  // the direct loads address an operand by 32-bit byte offsets from a row tile's base, an expert's
+  // K-major weight slice, or (rows gathered) the start of x: each of those spans must stay under 4 GiB
+  const unsigned long long lim = 1ull << 32, K = a.K, NO = a.Nout;
+  if (GBM * K * 2 >= lim || (a.bt && K * NO * 2 >= lim) ||
+      (a.gather && (unsigned long long)(a.n_rows_max + a.gather_div - 1) / a.gather_div * K * 2 >= lim))
+    return hipErrorNotSupported;
   // the up-projection tile pairs W1 and W3 rows (SwiGLU forward); every other form is a plain tile
   const bool dual = a.act == MOE_ACT_SWIGLU && a.epi != 2 && !a.bt;
   const int bno = dual ? GBR / 2 : GBR;
@@ -771,6 +814,7 @@ hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff
                              float* out0, float* out1, int split, hipStream_t s) {
   const long long tiles = (long long)G * ((M + GBM - 1) / GBM) * ((N + GBR - 1) / GBR);
   if (tiles == 0) return hipSuccess;
+  if ((unsigned long long)GBM * ld * 2 >= (1ull << 32)) return hipErrorNotSupported;  // 32-bit load offsets in a tile
   hipLaunchKernelGGL(ffn_wgrad_bf16, dim3((unsigned)tiles), dim3(GTH), 0, s, (const bf16_t*)aT, (const bf16_t*)bT,
                      koff, G, M, N, ld, out0, out1, split);
   return hipGetLastError();

@@ -55,7 +55,10 @@ int ffn_shape_ok(const moe_dims* d) {
   return d->D % 16 == 0 && d->F % 16 == 0;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+// hipErrorNotSupported is what a launcher returns for shapes its kernels cannot address
+int hip_status(hipError_t e) {
+  return e == hipSuccess ? MOE_OK : e == hipErrorNotSupported ? MOE_ERR_UNSUPPORTED : MOE_ERR_HIP;
+}
 
 size_t route_partial_rows(const moe_dims* d) {
   return ((size_t)d->T + moe::kRouteTokPerBlock - 1) / moe::kRouteTokPerBlock;

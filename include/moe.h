@@ -176,7 +176,10 @@ int moe_permute(const moe_dims* d, const void* x, const int32_t* pair_to_row, vo
  *   x_perm [T*top_k, D] in; w1, w3 [E,F,D]; w2 [E,D,F]; w3 may be NULL for MOE_ACT_GELU.
  *   y_perm [T*top_k, D] out (rows >= N untouched); ws: moe_workspace_size(MOE_STAGE_FFN) bytes.
  * bf16: matrix-core products with float32 accumulation; h is rounded to bf16 between the two
- * GEMMs; outputs rounded to nearest even. Unsupported: D or F not a multiple of 64. */
+ * GEMMs; outputs rounded to nearest even. Unsupported: D or F not a multiple of 64, or (bf16) an
+ * operand span of 4 GiB or more: 320 rows of x_perm, h or a weight matrix (320*D*2, 320*F*2 bytes)
+ * or one expert's weight matrix read K-major by the data-gradient forms (D*F*2, or 2*D*F*2 for
+ * W1 and W3), since the kernels address them with 32-bit offsets. */
 int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets,
                    const void* w1, const void* w3, const void* w2, void* y_perm, void* ws,
                    size_t ws_bytes, hipStream_t stream);
@@ -189,7 +192,9 @@ int moe_expert_ffn_up(const moe_dims* d, const void* x_perm, const int32_t* expe
 /* moe_permute followed by moe_expert_ffn_up in one launch: the up-projection reads row r straight from
  * x[row_to_pair[r] / top_k] ([EPLLM] pipeline steps 2 and 4 with the permuted copy of x left out).
  * Output identical bit for bit to the two calls. x [T,D] in; row_to_pair [T*top_k] int32 in (as
- * moe_dispatch_layout wrote it: entries [0, N) are read); h [T*top_k, F] out. */
+ * moe_dispatch_layout wrote it: entries [0, N) are read); h [T*top_k, F] out. Also unsupported
+ * (bf16): x of 4 GiB or more (T*D*2 bytes; the gathered rows are addressed by 32-bit offsets from
+ * x); pass x through moe_permute and moe_expert_ffn_up instead. */
 int moe_expert_ffn_up_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
                              const int32_t* expert_offsets, const void* w1, const void* w3, void* h,
                              hipStream_t stream);
@@ -355,7 +360,8 @@ int moe_expert_ffn_up_train(const moe_dims* d, const void* x_perm, const int32_t
                             const void* w1, const void* w3, void* h, void* pre, hipStream_t stream);
 
 /* moe_expert_ffn_up_train with its rows gathered from x (x_perm[r] = x[row_to_pair[r] / top_k], as
- * moe_expert_ffn_up_gather): the same h and pre, bit for bit, with no x_perm. */
+ * moe_expert_ffn_up_gather): the same h and pre, bit for bit, with no x_perm. Unsupported for x of
+ * 4 GiB or more, as moe_expert_ffn_up_gather. */
 int moe_expert_ffn_up_train_gather(const moe_dims* d, const void* x, const int32_t* row_to_pair,
                                    const int32_t* expert_offsets, const void* w1, const void* w3, void* h,
                                    void* pre, hipStream_t stream);
@@ -421,7 +427,9 @@ int moe_group_transpose_gather(const moe_dims* d, const void* x, int32_t n_cols,
 /* Per expert e: out_e[m, n] = sum over columns [koff[e], koff[e+1]) of a_t[m, col] * b_t[n, col]
  * (a_t [M, ld], b_t [N, ld] bf16, as moe_group_transpose writes them); rows m < split go to
  * out0 [E, split, N], the rest to out1 [E, M - split, N] (float32). dW2 = wgrad(dy_perm^T, h^T,
- * M = D, N = F); [dW1; dW3] = wgrad(da^T, x_perm^T, M = 2F (or F), N = D, split = F). */
+ * M = D, N = F); [dW1; dW3] = wgrad(da^T, x_perm^T, M = 2F (or F), N = D, split = F).
+ * MOE_ERR_UNSUPPORTED when 320 rows of a_t span 4 GiB or more (320*ld*2 bytes: the kernel's loads
+ * use 32-bit offsets within a tile). */
 int moe_expert_wgrad(const moe_dims* d, const void* a_t, const void* b_t, const int32_t* koff, int32_t M,
                      int32_t N, int64_t ld, float* out0, float* out1, int32_t split, hipStream_t stream);
 

@@ -103,6 +103,17 @@ def test_unsupported_shapes_reported():
     assert lib.moe_route(ctypes.byref(d), fake, fake, None, fake, fake, None, None) == M.MOE_ERR_UNSUPPORTED
     d = M.make_dims(16, 96, 8, 2, 64)                      # bf16 FFN needs D % 64 == 0
     assert lib.moe_expert_ffn_up(ctypes.byref(d), fake, fake, fake, fake, fake, None) == M.MOE_ERR_UNSUPPORTED
+    # the bf16 GEMMs address operands with 32-bit offsets: x of 4 GiB cannot be gathered from (the
+    # same x through x_perm is fine), nor can a weight-gradient tile span 4 GiB; both refused on the host
+    d = M.make_dims(1 << 19, 4096, 8, 2, 64)              # T*D*2 = 4 GiB
+    assert lib.moe_expert_ffn_up_gather(ctypes.byref(d), fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn_up_train_gather(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_UNSUPPORTED
+    d = M.make_dims(16, 64, 8, 2, 64)
+    ld = (1 << 32) // 640 // 64 * 64 + 64                  # 320 rows of ld bf16 columns reach 4 GiB
+    assert lib.moe_expert_wgrad(ctypes.byref(d), fake, fake, fake, 64, 64, ld, fake, None, 64, None) == \
+        M.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_checks():
