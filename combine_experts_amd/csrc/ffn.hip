@@ -304,13 +304,13 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
     if (i < G_NAL && i * (GTH / GKCH) >= mrows) return;
     bf16x8* dst = lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE;
     if (i < G_NAL) {
-      dma16(ds.a, ds.off[i], kt * GBK * 2, dst);
+      dma16(ds.a, ds.off[i], (uint32_t)kt * (GBK * 2), dst);
     } else if constexpr (BT) {
       const int k0 = kt * GBK;
       const bool lo = k0 < bt.ksplit;
-      dma16(lo ? ds.b0 : ds.b1, ds.off[i], (uint32_t)((lo ? k0 : k0 - bt.ksplit) * bt.nout * 2), dst);
+      dma16(lo ? ds.b0 : ds.b1, ds.off[i], (uint32_t)(lo ? k0 : k0 - bt.ksplit) * (uint32_t)bt.nout * 2u, dst);
     } else {
-      dma16(i < G_NAL + (G_LPS - G_NAL) / 2 ? ds.b0 : ds.b1, ds.off[i], kt * GBK * 2, dst);
+      dma16(i < G_NAL + (G_LPS - G_NAL) / 2 ? ds.b0 : ds.b1, ds.off[i], (uint32_t)kt * (GBK * 2), dst);
     }
   };
   bf16x8 fa[2][GMB], fb[2][2];
