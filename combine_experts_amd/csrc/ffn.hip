@@ -89,7 +89,7 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // rows of W1 and the matching 128 rows of W3, so the block produces 320 x 128 of h. Wave (wm, wn)
 // holds m-blocks {2i + wm} (32 rows each, interleaved so a ragged tile splits evenly between the
 // two wave rows) against 2 B blocks of 32 rows: 10 v_mfma_f32_32x32x16_bf16 per 16-deep k-step,
-// accumulators 5 x 2 x 16 floats (240-252 VGPRs, no spills). 320 rows rather than 256: an expert with
+// accumulators 5 x 2 x 16 floats (233-243 VGPRs, no spills). 320 rows rather than 256: an expert with
 // 2*256 + a few rows, common when routing is near even, needs two tiles instead of three, and every
 // tile re-streams the expert's weights. The weight fragment is the MFMA's first operand, so each lane
 // ends up with 4 consecutive output columns of one token row; the plain epilogue regroups them in LDS
