@@ -295,14 +295,14 @@ __device__ __forceinline__ FragIdx frag_idx(int lane, int wm, int wn) {
 }
 
 template <int ACT, bool BT>  // ACT: active 32-row blocks of this wave; BT: B stored K-major
-__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, const DmaSrc& ds,
+__device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds0, bf16x8* lds1, const DmaSrc& ds,
                                            const FragIdx& fi, const BtSrc& bt, int wave, int nk, int mrows) {
   // load i fills tile rows [i*64, i*64+64) of A (i < G_NAL) or a part of B (the first half of the B
   // loads from b0, the rest from b1); A loads wholly past the tile's rows are skipped (those rows
   // feed only accumulators that are never stored)
-  auto issue = [&](int kt, int buf, int i) {
+  auto issue = [&](int kt, bf16x8* slot, int i) {
     if (i < G_NAL && i * (GTH / GKCH) >= mrows) return;
-    bf16x8* dst = lds + buf * G_STAGE + i * GTH + wave * MOE_WAVE;
+    bf16x8* dst = slot + i * GTH + wave * MOE_WAVE;
     if (i < G_NAL) {
       dma16(ds.a, ds.off[i], (uint32_t)kt * (GBK * 2), dst);
     } else if constexpr (BT) {
@@ -314,8 +314,8 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
     }
   };
   bf16x8 fa[2][GMB], fb[2][2];
-  auto frag = [&](int buf, int ks, int r) {
-    const bf16x8* s = lds + buf * G_STAGE + fi.lane[ks];
+  auto frag = [&](const bf16x8* slot, int ks, int r) {
+    const bf16x8* s = slot + fi.lane[ks];
     if constexpr (!BT) {
       // in the order the next k-step's MFMAs take them (B0 A0, B1, then A1 ...), so that each MFMA
       // waits only for its own two fragments
@@ -330,7 +330,7 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
     for (int i = 0; i < ACT; ++i) fa[r][i] = s[fi.a + i * 2 * 32 * GKCH];
     if constexpr (BT) {
       // two transposed 8-byte reads per fragment: 4 consecutive k of this lane's column each
-      const char* sb = reinterpret_cast<const char*>(lds + buf * G_STAGE + G_ACH) + ks * 16 * GBR * 2;
+      const char* sb = reinterpret_cast<const char*>(slot + G_ACH) + ks * 16 * GBR * 2;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const bf16x4 lo = tr_read(sb + bt.tro[0][j]), hi = tr_read(sb + bt.tro[1][j]);
@@ -341,38 +341,32 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
   // the first stage's weight slices go first: their addresses need no row lookup, so their latency
   // overlaps that of the gathered row indices the A loads wait for
 #pragma unroll
-  for (int i = G_NAL; i < G_LPS; ++i) issue(0, 0, i);
+  for (int i = G_NAL; i < G_LPS; ++i) issue(0, lds0, i);
 #pragma unroll
-  for (int i = 0; i < G_NAL; ++i) issue(0, 0, i);
+  for (int i = 0; i < G_NAL; ++i) issue(0, lds0, i);
   wait_vmcnt<0>();
   __syncthreads();
-  frag(0, 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
+  frag(lds0, 0, 0);
+  // the two ring slots are two LDS arrays and the loop body is written out once per slot, so every
+  // load and fragment read names its slot: the compiler then knows that a stage's reads (slot cur)
+  // and the next stage's loads (slot nxt) do not overlap
+  auto stage = [&](int kt, bf16x8* cur, bf16x8* nxt) {
     const bool refill = kt + 1 < nk;
 #pragma unroll
     for (int ks = 0; ks < G_KS; ++ks) {
       const int c = ks & 1, n = c ^ 1;
       // all of stage kt+1 goes to the other slot at once (free since the barrier that ended iteration
-      // kt-1), at the start of stage kt: the loads get a whole stage to land. The transposed reads of
-      // the BT form count, for the compiler, as possibly reading what those loads write, so there the
-      // loads go out after the stage's last fragment read instead (else each stage would wait for
-      // them right after issuing them)
-      constexpr int ISSUE_KS = BT ? G_KS - 2 : 0;
-      if (!BT && refill && ks == ISSUE_KS) {
+      // kt-1), at the start of stage kt: the loads get a whole stage to land
+      if (refill && ks == 0) {
 #pragma unroll
-        for (int i = 0; i < G_LPS; ++i) issue(kt + 1, buf ^ 1, i);
+        for (int i = 0; i < G_LPS; ++i) issue(kt + 1, nxt, i);
       }
       if (ks < G_KS - 1) {
-        frag(buf, ks + 1, n);
-        if (BT && refill && ks == ISSUE_KS) {
-#pragma unroll
-          for (int i = 0; i < G_LPS; ++i) issue(kt + 1, buf ^ 1, i);
-        }
+        frag(cur, ks + 1, n);
       } else if (refill) {
         wait_vmcnt<0>();  // this wave's part of stage kt+1 has landed ...
-        __syncthreads();  // ... and everyone's; everyone is also done reading slot buf
-        frag(buf ^ 1, 0, n);
+        __syncthreads();  // ... and everyone's; everyone is also done reading slot cur
+        frag(nxt, 0, n);
       }
 #pragma unroll
       for (int i = 0; i < ACT; ++i)
@@ -391,6 +385,10 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds, c
         if constexpr (NM > NP) __builtin_amdgcn_sched_group_barrier(0x008, NM - NP, 0);
       }
     }
+  };
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage(kt, lds0, lds1);
+    if (kt + 1 < nk) stage(kt + 1, lds1, lds0);
   }
 }
 
@@ -419,7 +417,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
                                                      int gdiv, int ksplit) {
   static_assert(!(BT && DUAL), "the K-major B form has no paired W1/W3 tile");
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
-  __shared__ bf16x8 lds[2 * G_STAGE];
+  __shared__ bf16x8 lds0[G_STAGE], lds1[G_STAGE];  // the two slots of the K ring
   const int NT = (Nout + BNO - 1) / BNO;
   int e, mt, nt, o0, cnt;
   if (!map_tile_xcd(offsets, E, NT, &e, &mt, &nt, &o0, &cnt)) return;
@@ -489,11 +487,11 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const int nk = K / GBK;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
-    case 5: gemm_kloop<5, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
-    case 4: gemm_kloop<4, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
-    case 3: gemm_kloop<3, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
-    case 2: gemm_kloop<2, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
-    default: gemm_kloop<1, BT>(acc, lds, ds, fi, bt, wave, nk, mrows); break;
+    case 5: gemm_kloop<5, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
+    case 4: gemm_kloop<4, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
+    case 3: gemm_kloop<3, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
+    case 2: gemm_kloop<2, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
+    default: gemm_kloop<1, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
   constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
@@ -503,7 +501,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     // WC/8 lanes per row, instead of 8-byte pieces of 32 rows per instruction
     constexpr int WC = DUAL ? 32 : 64;  // output columns per wave
     constexpr int SROW = WC + 8;        // staging row stride (elements; rows stay 16-byte aligned)
-    bf16_t* stg = reinterpret_cast<bf16_t*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROW;
+    bf16_t* stg = reinterpret_cast<bf16_t*>((nk & 1) ? lds1 : lds0) + wave * 32 * SROW;
     const int cw = DUAL ? wn * 32 : wn * 64;
 #pragma unroll
     for (int i = 0; i < GMB; ++i) {
@@ -544,7 +542,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   constexpr int SROWF = 64 + 4;                  // staging row stride (floats; rows stay 16-byte aligned)
   constexpr int OCW = DUAL ? 32 : 64;            // output columns per wave
   constexpr int LPR = OCW / 8, RPI = MOE_WAVE / LPR;
-  float* stg = reinterpret_cast<float*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROWF;
+  float* stg = reinterpret_cast<float*>((nk & 1) ? lds1 : lds0) + wave * 32 * SROWF;
   const int cw = DUAL ? wn * 32 : wn * 64;
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
@@ -619,7 +617,7 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
                                                       const int32_t* __restrict__ koff, int G, int M, int N,
                                                       long long ld, float* __restrict__ out0,
                                                       float* __restrict__ out1, int split) {
-  __shared__ bf16x8 lds[2 * G_STAGE];
+  __shared__ bf16x8 lds0[G_STAGE], lds1[G_STAGE];  // the two slots of the K ring
   const int MT = (M + GBM - 1) / GBM, NT = (N + GBR - 1) / GBR;
   const int per_g = MT * NT;
   const int t = blockIdx.x;
@@ -657,12 +655,12 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  if (nk > 0) gemm_kloop<GMB, false>(acc, lds, ds, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
+  if (nk > 0) gemm_kloop<GMB, false>(acc, lds0, lds1, ds, fi, BtSrc{}, wave, nk, mrows);  // uniform: an empty group writes zeros
   // the tile goes out through LDS: each wave stages its 32-row blocks (32 x 64 floats) in the ring slot
   // the last stage did not read and stores 256-byte row pieces, 16 lanes per row, instead of 16-byte
   // pieces of 32 rows per instruction
   constexpr int SROW = 64 + 4;  // staging row stride (floats; rows stay 16-byte aligned)
-  float* stg = reinterpret_cast<float*>(lds + (nk & 1) * G_STAGE) + wave * 32 * SROW;
+  float* stg = reinterpret_cast<float*>((nk & 1) ? lds1 : lds0) + wave * 32 * SROW;
 #pragma unroll
   for (int i = 0; i < GMB; ++i) {
 #pragma unroll
