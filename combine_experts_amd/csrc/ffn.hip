@@ -363,10 +363,12 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds0, 
       }
       if (ks < G_KS - 1) {
         frag(cur, ks + 1, n);
-      } else if (refill) {
+      } else {
+        // also after the last stage, so that no path through the loop leaves a load in flight at
+        // its head (the compiler would otherwise wait for loads before the first stage's reads)
         wait_vmcnt<0>();  // this wave's part of stage kt+1 has landed ...
         __syncthreads();  // ... and everyone's; everyone is also done reading slot cur
-        frag(nxt, 0, n);
+        if (refill) frag(nxt, 0, n);
       }
 #pragma unroll
       for (int i = 0; i < ACT; ++i)
