@@ -553,8 +553,8 @@ def router_probabilities(l: np.ndarray, gate: int) -> np.ndarray:
     """Router probability of every expert for every token (all E, before top-k).
 
     Softmax over the E logits for softmax gates; the sigmoid scores
-    normalised over all E for sigmoid gates (READING: the pages define P_i
-    only as the router probability allocated to expert i).
+    normalised over all E for sigmoid gates (READING: the pages give P_i no
+    formula beyond naming it expert i's router probability).
     """
     l = np.asarray(l, dtype=np.float64)
     if gate == GATE_SIGMOID_TOPK:
@@ -569,10 +569,10 @@ def load_balance_stats(expert_counts: np.ndarray, probs: np.ndarray, k: int, alp
     """Auxiliary load-balancing loss L_aux = alpha * E * sum_i f_i * P_i.
 
     [EPLLM] "Static Capacity Factors and Token Dropping", auxiliary-loss
-    equation: f_i the fraction of tokens dispatched to expert i, P_i the
-    router probability allocated to expert i. READING: f_i = c_i / (T*k)
-    (the share of (token, expert) pairs, before any capacity cut) and
-    P_i = mean over tokens of router_probabilities. Also returns the
+    equation. f_i is expert i's share of the routed pairs and P_i its mean
+    router probability. READING: f_i = c_i / (T*k) (pairs counted before
+    any capacity cut) and P_i = mean over tokens of router_probabilities.
+    Also returns the
     imbalance max_i c_i / mean_i c_i ([EPA2A] "When it breaks": one expert
     with several times its share stalls the layer).
     """

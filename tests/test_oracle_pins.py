@@ -177,6 +177,89 @@ def test_decisive_flags_near_ties():
     assert d["order"].tolist() == [False, True, False]
 
 
+# Group-limited decisive flags. 12 experts in 4 contiguous groups of 3, k = 4, 2 groups kept, so a
+# group scores the sum of its 2 best members (k / kept groups). Margins are hand-placed so that
+# exactly one comparison falls below 1e-3 in each token.
+_G = dict(k=4, margin=1e-3, n_groups=4, topk_groups=2)
+
+
+def test_decisive_group_margin_alone_decides():
+    # softmax gating (group scores on logits): groups score 10, 8, 7.9995, 2 -> kept {0, 1}, and the
+    # last kept (8) vs first dropped (7.9995) margin is 5e-4; the expert margin inside the kept groups
+    # (4th best 3 vs 5th best 0) is 3. Control token: the third group scores 7.998 (margin 2e-3).
+    l = np.array([[6, 4, 0, 5, 3, -1, 4.5, 3.4995, -3, 1, 1, -5],
+                  [6, 4, 0, 5, 3, -1, 4.5, 3.498, -3, 1, 1, -5]], dtype=np.float64)
+    d = O.decisive_tokens(l, gate=O.GATE_SOFTMAX_TOPK, **_G)
+    assert d["set"].tolist() == [False, True]
+    assert d["order"].tolist() == [False, True]       # top 4 = 6, 5, 4, 3: adjacent margins all 1
+
+
+def test_decisive_expert_margin_counts_eligible_experts_only():
+    # groups score 10, 8, 2, 1 (kept {0, 1}, margin 6).
+    # token 0: inside the kept groups the 4th and 5th best logits are 3.0004 and 3 -> not decisive.
+    # token 1: the near-tie partner 3.0004 sits in a dropped group (group 2 scores 3.0004 - 5 < 8),
+    #          so among eligible experts the 4th vs 5th margin is 3 - 0 = 3 -> decisive.
+    l = np.array([[6, 4, 3.0004, 5, 3, -1, 1, 1, 0, 0.5, 0.5, 0],
+                  [6, 4, 0, 5, 3, -1, 3.0004, -5, -5, 0.5, 0.5, 0]], dtype=np.float64)
+    d = O.decisive_tokens(l, gate=O.GATE_SOFTMAX_TOPK, **_G)
+    assert d["set"].tolist() == [False, True]
+    # without the group limit token 1 would tie within 4e-4 (4th 3.0004 vs 5th 3)
+    assert O.decisive_tokens(l, 4, 1e-3)["set"].tolist() == [False, False]
+
+
+def test_decisive_group_scores_use_sigmoid_scores_under_sigmoid_gating():
+    # logits per group: [10, 9, 0], [6, 6, 5.9996], [20, 2, -3], [-1, -1, -2]
+    # sigmoid group scores (sum of the 2 best sigmoids) 1.99983, 1.99505, 1.88080, 0.53788 -> keep {0, 1};
+    #   eligible logits 10, 9, 6, 6, 5.9996 -> 4th vs 5th margin 4e-4 -> not decisive
+    # logit group scores 19, 12, 22, -2 -> keep {2, 0}; eligible 20, 10, 9, 2, 0 -> decisive
+    l = np.array([[10, 9, 0, 6, 6, 5.9996, 20, 2, -3, -1, -1, -2]], dtype=np.float64)
+    sig = 1.0 / (1.0 + np.exp(-l))
+    _, kept_sig = O.select_group_limited(l, 4, 4, 2, sig)
+    _, kept_log = O.select_group_limited(l, 4, 4, 2, l)
+    assert kept_sig.tolist() == [[0, 1]] and kept_log.tolist() == [[2, 0]]
+    assert O.decisive_tokens(l, gate=O.GATE_SIGMOID_TOPK, **_G)["set"].tolist() == [False]
+    assert O.decisive_tokens(l, gate=O.GATE_SOFTMAX_TOPK, **_G)["set"].tolist() == [True]
+    # a sigmoid near-tie between groups that is wide in logit space: [8, 8] vs [7.5, 9.5] score
+    # 1.999329 vs 1.999372 as sigmoids (4.3e-5 apart), 16 vs 17 as logits
+    l2 = np.array([[10, 9, 0, 8, 8, 0, 7.5, 9.5, 0, -1, -1, -2]], dtype=np.float64)
+    assert O.decisive_tokens(l2, gate=O.GATE_SIGMOID_TOPK, **_G)["set"].tolist() == [False]
+    assert O.decisive_tokens(l2, gate=O.GATE_SOFTMAX_TOPK, **_G)["set"].tolist() == [True]
+
+
+@pytest.mark.parametrize("gate", [O.GATE_SOFTMAX_TOPK, O.GATE_SIGMOID_TOPK])
+def test_decisive_tokens_keep_their_selection_under_perturbation(gate):
+    # Brute force: a token flagged decisive must select the same experts (and, when flagged for order,
+    # in the same slots) after any perturbation of its logits by at most margin/8. That moves a
+    # difference of two logits by at most margin/4 and a difference of two group scores (each a sum of
+    # two members) by at most margin/2; a sigmoid moves by at most a quarter of its argument's change.
+    rng = np.random.default_rng(21)
+    T, E, k, ng, tg, margin = 300, 12, 4, 4, 2, 1e-3
+    # logits on a 5e-4 grid in a narrow range: many comparisons sit at 0, 5e-4 or 1e-3 apart
+    l = rng.integers(-6, 7, size=(T, E)) * 5e-4 + rng.integers(-1, 2, size=(T, E)) * 0.01
+    d = O.decisive_tokens(l, k, margin, ng, tg, gate)
+    assert 0.05 < d["set"].mean() < 0.95                 # both kinds are present
+
+    def sel(v):
+        score = 1.0 / (1.0 + np.exp(-v)) if gate == O.GATE_SIGMOID_TOPK else v
+        # selection in float64 (no float32 rounding) so that only the perturbation moves it
+        gs = O.group_scores(score, ng, k // tg)
+        gorder = np.argsort(-gs, axis=1, kind="stable")[:, :tg]
+        elig = np.zeros(v.shape, dtype=bool)
+        for j in range(tg):
+            for m in range(E // ng):
+                elig[np.arange(len(v)), gorder[:, j] * (E // ng) + m] = True
+        return O.select_topk(v, k, elig)
+
+    base = sel(l)
+    delta = margin / 8
+    for _ in range(200):
+        pert = l + rng.choice([-delta, 0.0, delta], size=l.shape)
+        got = sel(pert)
+        s, o = d["set"], d["order"]
+        assert np.array_equal(np.sort(got[s], axis=1), np.sort(base[s], axis=1))
+        assert np.array_equal(got[o], base[o])
+
+
 # ------------------------------------------------------------------------------------------------
 # Dispatch layout
 # ------------------------------------------------------------------------------------------------
@@ -300,8 +383,29 @@ def test_remote_fraction_uniform_routing():
     lay = O.dispatch_layout(idx, E, N)
     remote = lay["n_kept"] - lay["rank_counts"][0]
     assert abs(remote / (T * k) - (N - 1) / N) < 0.01
-    vol = O.dispatch_volume_bytes(remote, 4096, 2)
-    assert vol == remote * 4096 * 2
+
+
+def test_dispatch_volume_matches_the_page_equation_on_exactly_uniform_routing():
+    # Per-GPU dispatch volume B*S*k*H*(EP-1)/EP*sizeof ("Communication Volume and Hardware Topology").
+    # B=2, S=4 (T=8 tokens), k=2, E=8 experts on EP=4 devices (2 each), H=16, bf16 (2 bytes).
+    # Pair p = t*k + j goes to expert p mod 8, so each device receives exactly T*k/EP = 4 pairs and,
+    # seen from any one device, 16 - 4 = 12 pairs leave it: 2*4*2*16*(3/4)*2 = 384 bytes.
+    T, k, E, EP, H = 8, 2, 8, 4, 16
+    idx = (np.arange(T * k) % E).reshape(T, k)
+    lay = O.dispatch_layout(idx, E, EP)
+    assert lay["rank_counts"].tolist() == [4, 4, 4, 4]
+    for r in range(EP):
+        remote = lay["n_kept"] - lay["rank_counts"][r]
+        assert O.dispatch_volume_bytes(remote, H, 2) == 384
+    # every pair already on device 0: nothing leaves it; every pair on device 3: all 16 pairs leave
+    # device 0 (16 * 16 * 2 = 512 bytes) and nothing leaves device 3
+    local = O.dispatch_layout(np.zeros((T, k), dtype=np.int64), E, EP)
+    assert O.dispatch_volume_bytes(local["n_kept"] - local["rank_counts"][0], H, 2) == 0
+    far = O.dispatch_layout(np.full((T, k), 7), E, EP)
+    assert O.dispatch_volume_bytes(far["n_kept"] - far["rank_counts"][0], H, 2) == 512
+    assert O.dispatch_volume_bytes(far["n_kept"] - far["rank_counts"][3], H, 2) == 0
+    # float32 doubles it (sizeof = 4): 768 bytes on the uniform routing
+    assert O.dispatch_volume_bytes(lay["n_kept"] - lay["rank_counts"][1], H, 4) == 768
 
 
 # ------------------------------------------------------------------------------------------------
