@@ -5,9 +5,12 @@ for it (the saved forward tensors and the previous backward step's output), so i
 differences never enter: dy_perm and dgate, the activation backward da, dx_perm, the router's dl,
 dW_g and dbias, the final dx, the transposes (bit for bit) and the three weight gradients. dx is also
 compared end to end with the oracle's float64 layer backward on decisive tokens.
-Tolerances: bf16 outputs 2e-2 per row relative to the row's largest reference entry (one bf16
-rounding of an fp32 sum is 2^-9, the operands carry one rounding each); float32 outputs
-(dgate, dl, dW_g, dbias, weight gradients) 1e-3 relative to the largest reference entry.
+Every gradient is then compared with the oracle's float64 layer backward (O.layer_backward) run on
+the GPU's own routing, layout, logits, x_perm and y_perm.
+Tolerances: bf16 outputs 2e-2 per row relative to the row's largest reference entry (the bound the
+layer output has); float32 outputs (dgate, dl, dW_g, dbias) 1e-3 relative to the largest reference
+entry; weight gradients element by element within a first-order bound of the GPU's roundings and
+within 2e-2 of the largest entry (TOL_WG_SUM, TOL_WG and _perturbation_scale below).
 """
 import numpy as np
 import pytest
@@ -24,6 +27,38 @@ needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GP
 
 TOL_ROW = 2e-2
 TOL_F32 = 1e-3
+# weight gradients: each is a sum over an expert's rows of products whose GPU operands carry bf16
+# roundings; each rounding moves its value by at most 2^-8 relative (bf16 keeps 8 significant bits,
+# round to nearest), and _perturbation_scale adds up, to first order, what every rounding on the way to
+# an operand can move it by (in units of 2^-8). TOL_WG_SUM allows twice that (the float32 sums add
+# ~1e-6 relative). TOL_WG: the largest error within 2e-2 of the expert's largest entry, the bound of
+# the layer's bf16 output
+TOL_WG_SUM = 2 * 2.0 ** -8
+TOL_WG = 2e-2
+SILU2_MAX, GELU2_MAX = 0.5, 0.8   # max |SiLU''| = 0.5 (at 0), max |GELU''| = 2 phi(0) = 0.798
+
+
+def _perturbation_scale(ob, host, cfg, e, lo, hi):
+    """First-order bounds, in units of 2^-8, on how far the GPU's bf16 roundings move the left operands
+    of expert e's weight gradients: dy_perm (rounded once) for dW2; da1 and da3 for dW1, dW3.
+    da1 = dh * a3 * SiLU'(a1) (GELU: dh * GELU'(a1)) and da3 = dh * SiLU(a1) are formed from dh, a sum
+    over dy_perm rows (each rounded: |d dh| <= sum |dy_perm||W2| =: dh_abs), the stored pre-activations
+    a1, a3 (rounded: |d a| <= |a|, and f(a1) moves by at most max|f''| |a1| for f = SiLU', or max|f'| for
+    f = SiLU), and are rounded once more themselves."""
+    dyp = np.abs(ob["dy_perm"][lo:hi])
+    dh = ob["dh"][lo:hi]
+    a1 = ob["a1"][lo:hi]
+    dh_abs = dyp @ np.abs(O.as_f64(host["w2"][e]))
+    if cfg.act == W.ACT_SWIGLU:
+        a3 = ob["a3"][lo:hi]
+        s1 = O.silu_grad(a1)
+        m1 = dh_abs * np.abs(a3 * s1) + 2 * np.abs(dh * a3 * s1) + SILU2_MAX * np.abs(dh * a3 * a1)
+        m3 = dh_abs * np.abs(O.silu(a1)) + 1.1 * np.abs(dh * a1) + np.abs(dh * O.silu(a1))
+    else:
+        g1 = O.gelu_grad(a1)
+        m1 = dh_abs * np.abs(g1) + GELU2_MAX * np.abs(dh * a1) + np.abs(dh * g1)
+        m3 = None
+    return 2 * dyp, m1, m3
 
 CASES = {
     "mixtral_small": W.get_config("mixtral", T=512, D=512, F=448),
@@ -241,7 +276,50 @@ def test_backward_stages(name):
         if nm == 2:
             assert _scaled(P.f64(dw3[e]), da_h[lo:hi, F:].T @ xp[lo:hi]) <= TOL_F32, f"dW3 expert {e}"
 
-    # end to end: dx against the oracle's float64 backward on decisive tokens (dropless only)
+    # The pinned oracle as the checker: O.layer_backward on a forward record that holds the GPU's own
+    # routing, layout, logits, x_perm and y_perm (staged), so every token compares, drops included.
+    fwd_g = {"pair_to_row": p2r, "row_to_pair": P.i64(buf.row_to_pair), "expert_offsets": off,
+             "topk_gate": gates.reshape(T, k), "topk_idx": idx, "logits": l_gpu,
+             "y_perm": P.f64(buf.y_perm), "x_perm": P.f64(buf.x_perm)}
+    ob = O.layer_backward(host, cfg, fwd_g, dyh)
+    errs = {"dy_perm": _rel(dyp_h, ob["dy_perm"]).max(),
+            "da1": _rel(da_h[:, :F], ob["da1"]).max(),
+            "dx_perm": _rel(dxp_h, ob["dx_perm"]).max(),
+            "dx": _rel(P.f64(dx), ob["dx"]).max(),
+            "dgate": _scaled(dg.reshape(T, k)[p2r.reshape(T, k) >= 0], ob["dgate"][p2r.reshape(T, k) >= 0]),
+            "dl": _scaled(dl_h, ob["dl"]), "dw_gate": _scaled(P.f64(dwg), ob["dw_gate"]),
+            "dbias": _scaled(P.f64(dbias), ob["dbias"])}
+    if nm == 2:
+        errs["da3"] = _rel(da_h[:, F:], ob["da3"]).max()
+    for key in ("dy_perm", "da1", "da3", "dx_perm", "dx"):
+        if key in errs:
+            assert errs[key] <= TOL_ROW, f"{key} vs the oracle's backward: {errs[key]:.3e}"
+    for key in ("dgate", "dl", "dw_gate", "dbias"):
+        assert errs[key] <= TOL_F32, f"{key} vs the oracle's backward: {errs[key]:.3e}"
+    # weight gradients element by element: |got - ref| <= TOL_WG_SUM * (M^T |B|), M the first-order
+    # magnitude of the GPU's rounding perturbations of the left operand (_perturbation_scale), B the
+    # right operand (h for dW2, x_perm for dW1/dW3); and within TOL_WG of the expert's largest entry
+    wg_err = 0.0
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        m2, m1, m3 = _perturbation_scale(ob, host, cfg, e, lo, hi)
+        pairs = [("dw2", dw2[e], ob["dw2"][e], m2, ob["h"][lo:hi]),
+                 ("dw1", dw1[e], ob["dw1"][e], m1, xp[lo:hi])]
+        if nm == 2:
+            pairs.append(("dw3", dw3[e], ob["dw3"][e], m3, xp[lo:hi]))
+        for key, got, ref, A, B in pairs:
+            got = P.f64(got)
+            bound = TOL_WG_SUM * (A.T @ np.abs(B))
+            assert np.all(np.abs(got - ref) <= bound + 1e-30), f"{key} expert {e} vs the oracle: elementwise bound"
+            sc = _scaled(got, ref)
+            assert sc <= TOL_WG, f"{key} expert {e} vs the oracle's backward: {sc:.3e}"
+            wg_err = max(wg_err, sc)
+    print(f"[backward] {name}: vs O.layer_backward " + ", ".join(f"{k_} {v:.1e}" for k_, v in errs.items())
+          + f", weight gradients {wg_err:.1e}", flush=True)
+
+    # end to end: dx against the oracle's own float64 forward + backward on decisive tokens (dropless)
     if cfg.capacity_factor <= 0:
         fwd = O.layer_forward(host, cfg)
         bwd = O.layer_backward(host, cfg, fwd, dyh)
@@ -249,7 +327,7 @@ def test_backward_stages(name):
         same = (fwd["topk_idx"] == idx).all(axis=1) & dec
         assert same.mean() > 0.5
         err = P.rel_err_rows(P.f64(dx)[same], bwd["dx"][same])
-        assert err.max() <= 5e-2, f"dx end to end: max rel err {err.max():.3e}"
+        assert err.max() <= TOL_ROW, f"dx end to end: max rel err {err.max():.3e}"
         print(f"[backward] {name}: dx end-to-end max rel err {err.max():.2e} on {same.sum()} tokens", flush=True)
 
 

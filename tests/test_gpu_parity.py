@@ -66,6 +66,28 @@ def test_small_all_stages(name):
 
 
 @needs_gpu
+@pytest.mark.parametrize("name", ["tiny_fp32", "switch_cap", "mixtral_small", "dsv3_small", "odd_f32", "cap_k2"])
+def test_expert_ffn_single_call(name):
+    """moe_expert_ffn (both FFN halves, h in the caller's workspace) against the oracle's expert FFN on
+    the GPU's own x_perm and offsets, element by element; the same bits as the two halves in turn."""
+    cfg = SMALL[name]
+    print(f"[parity] moe_expert_ffn {name}: {cfg}", flush=True)
+    inp = W.make_inputs(cfg, "cuda")
+    host = P.to_host(inp)
+    d, buf = P.run_gpu(cfg, inp)
+    ws = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_FFN), dtype=torch.uint8, device="cuda")
+    y_perm = torch.zeros_like(buf.y_perm)
+    M.moe_expert_ffn(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], inp["w2"], y_perm, ws)
+    torch.cuda.synchronize()
+    N = int(buf.expert_offsets[-1])
+    assert torch.equal(y_perm[:N], buf.y_perm[:N]), "moe_expert_ffn differs from up + down"
+    off = P.i64(buf.expert_offsets)
+    ref = O.expert_ffn(P.f64(buf.x_perm[:N]), off, host["w1"], host["w3"], host["w2"], cfg.act)
+    err = P.rel_err_rows(P.f64(y_perm[:N]), ref[:N])
+    assert err.max(initial=0.0) <= P.TOL_Y[cfg.dtype], f"moe_expert_ffn: max rel err {err.max():.3e}"
+
+
+@needs_gpu
 @pytest.mark.parametrize("name", ["mixtral_small", "dsv3_small", "cap_k2"])
 def test_deterministic_rerun(name):
     cfg = SMALL[name]
@@ -219,15 +241,42 @@ def test_full_size_sampled(name):
     toks = rng.choice(cfg.T, size=min(1024, cfg.T), replace=False)
     P.check_combine_tokens(cfg, buf, toks)
     P.check_identity_experts(cfg, buf, inp["x"])
-    # end to end on a few decisive tokens whose experts were all sampled above
+    wcache.clear()
+    # end to end against the oracle's float64 layer on E2E_TOKENS random decisive tokens, topped up so
+    # that every expert serves at least one of them (dropless workloads: with a capacity a flipped route
+    # elsewhere can change who is dropped, so switch_cap is compared staged only)
     if cfg.capacity_factor <= 0:
-        picked = set(e for (_, e) in wcache)
-        cand = [t for t in np.nonzero(dec["set"])[0] if set(r["topk_idx"][t].tolist()) <= picked][:8]
-        if not cand:
-            cand = list(np.nonzero(dec["set"])[0][:2])
-        for t in cand:
-            xr = np.repeat(O.as_f64(host["x"][t:t + 1]), cfg.top_k, axis=0)
-            outs = O.expert_ffn_rows(xr, r["topk_idx"][t], hw["w1"], hw["w3"], hw["w2"], cfg.act)
-            ref = (r["topk_gate"][t][:, None] * outs).sum(axis=0, keepdims=True)
-            err = P.rel_err_rows(P.f64(buf.y[t:t + 1]), ref)
-            assert err.max() <= P.TOL_Y[cfg.dtype], f"end-to-end token {t}: {err.max():.3e}"
+        toks = _e2e_tokens(r["topk_idx"], dec["set"], cfg.E, rng)
+        print(f"[parity-full] end to end on {len(toks)} decisive tokens", flush=True)
+        idx_t, g_t = r["topk_idx"][toks], r["topk_gate"][toks]
+        xr = O.as_f64(host["x"][torch.as_tensor(toks)])
+        ref = np.zeros((len(toks), cfg.D))
+        for e in np.unique(idx_t):
+            ti, sj = np.nonzero(idx_t == e)
+            # one expert's weights at a time, upcast exactly to float64
+            we = {key: (None if inp[key] is None else inp[key][e].double().cpu().numpy()) for key in ("w1", "w3", "w2")}
+            out = O.expert_ffn_rows(xr[ti], np.full(len(ti), e), lambda _e: we["w1"],
+                                    None if we["w3"] is None else (lambda _e: we["w3"]), lambda _e: we["w2"], cfg.act)
+            ref[ti] += g_t[ti, sj][:, None] * out
+        err = P.rel_err_rows(P.f64(buf.y[torch.as_tensor(toks, device=buf.y.device)]), ref)
+        print(f"[parity-full] end to end max rel err {err.max():.3e}", flush=True)
+        assert err.max() <= P.TOL_Y[cfg.dtype], f"end to end: max rel err {err.max():.3e}"
+
+
+E2E_TOKENS = 256
+
+
+def _e2e_tokens(topk_idx, decisive, E, rng):
+    """E2E_TOKENS random decisive tokens plus, for any expert none of them uses, one more decisive token
+    routed to it (when one exists)."""
+    cand = np.nonzero(decisive)[0]
+    toks = set(rng.choice(cand, size=min(E2E_TOKENS, cand.size), replace=False).tolist())
+    covered = set(topk_idx[sorted(toks)].reshape(-1).tolist())
+    for e in range(E):
+        if e in covered:
+            continue
+        hit = cand[(topk_idx[cand] == e).any(axis=1)]
+        if hit.size:
+            toks.add(int(hit[0]))
+            covered |= set(topk_idx[hit[0]].tolist())
+    return np.array(sorted(toks))
