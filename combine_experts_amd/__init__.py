@@ -7,7 +7,8 @@ built in-tree by ``python -m combine_experts_amd.build``.
 from ._lib import (  # noqa: F401
     MoEError, moe_dims, make_dims, dims_from_config, load_library, LIB_PATH,
     moe_abi_version, moe_status_str, moe_capacity, moe_workspace_size, moe_route, moe_route_ex,
-    moe_load_balance, moe_dispatch_layout, moe_dispatch_matrix, moe_recv_layout, moe_gather_rows, moe_scatter_rows,
+    moe_load_balance, moe_dispatch_layout, moe_dispatch_layout_noalloc, MOE_LAYOUT_NOALLOC_SCRATCH_BYTES,
+    moe_dispatch_matrix, moe_recv_layout, moe_gather_rows, moe_scatter_rows,
     moe_padded_layout, moe_permute_padded, moe_expert_ffn_padded_up, moe_expert_ffn_padded_down,
     moe_unpermute_combine_add, moe_layer_forward, moe_layer_args, moe_event_create, moe_event_destroy,
     moe_expert_ffn_up_train, moe_expert_ffn_up_train_gather, moe_group_transpose_gather, moe_transpose_weights, moe_backward_combine, moe_expert_ffn_down_backward,

@@ -99,6 +99,7 @@ _SIG = {
     "moe_layer_backward": (ctypes.c_int, [ctypes.POINTER(moe_dims), ctypes.POINTER(moe_backward_args), _P]),
     "moe_dispatch_layout": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            ctypes.c_size_t, _P]),
+    "moe_dispatch_layout_noalloc": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_permute": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P]),
     "moe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_expert_ffn_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
@@ -241,6 +242,22 @@ def moe_dispatch_layout(d: moe_dims, topk_idx, expert_counts, expert_offsets, ra
         _ptr(row_to_pair, "row_to_pair", i32, P), _ptr(ws, "ws", nullable=True),
         0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check("moe_dispatch_layout", st)
+
+
+MOE_LAYOUT_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+
+def moe_dispatch_layout_noalloc(d: moe_dims, topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets,
+                                pair_to_row, row_to_pair, stream=None) -> None:
+    """moe_dispatch_layout with its scratch in the library's static per-GPU array (no workspace)."""
+    P = d.T * d.top_k
+    i32 = torch.int32
+    st = load_library().moe_dispatch_layout_noalloc(
+        ctypes.byref(d), _ptr(topk_idx, "topk_idx", i32, P), _ptr(expert_counts, "expert_counts", i32, d.E),
+        _ptr(expert_offsets, "expert_offsets", i32, d.E + 1), _ptr(rank_counts, "rank_counts", i32, d.ep_size),
+        _ptr(rank_offsets, "rank_offsets", i32, d.ep_size + 1), _ptr(pair_to_row, "pair_to_row", i32, P),
+        _ptr(row_to_pair, "row_to_pair", i32, P), _stream(stream))
+    _check("moe_dispatch_layout_noalloc", st)
 
 
 def moe_permute(d: moe_dims, x, pair_to_row, x_perm, stream=None) -> None:

@@ -17,6 +17,14 @@
 //                  (wave ballots find same-expert lanes); row = offset + rank if rank < capacity.
 #include "moe_common.h"
 
+#include <mutex>
+
+// Per-chunk histograms of moe_dispatch_layout_noalloc: a static array of this library instead of a
+// caller workspace, for callers that cannot allocate. Every GPU the library runs on holds its own
+// copy until the process ends; all calls on one GPU share it. In host code this name only stands in
+// for the array: its device address comes from hipGetSymbolAddress (layout_noalloc_scratch below).
+static __device__ __align__(256) int32_t scratch[MOE_LAYOUT_NOALLOC_SCRATCH_BYTES / sizeof(int32_t)];
+
 namespace moe {
 namespace {
 
@@ -169,6 +177,27 @@ __global__ void __launch_bounds__(256) layout_assign(const int32_t* __restrict__
 size_t layout_ws_bytes(int32_t n_pairs, int32_t E) {
   const size_t n_chunks = (size_t)(n_pairs + kLayoutChunk - 1) / kLayoutChunk;
   return (n_chunks > 0 ? n_chunks : 1) * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t layout_noalloc_scratch(int32_t** out) {
+  // looked up once per device, with that device current, and kept: each GPU's copy of the array
+  // sits at its own address
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s) {

@@ -160,6 +160,25 @@ int moe_dispatch_layout(const moe_dims* d, const int32_t* topk_idx, int32_t* exp
   return hip_status(moe::launch_layout(a, stream));
 }
 
+int moe_dispatch_layout_noalloc(const moe_dims* d, const int32_t* topk_idx, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* pair_to_row, int32_t* row_to_pair, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (!expert_counts || !expert_offsets || !rank_counts || !rank_offsets) return MOE_ERR_INVALID_ARG;
+  if (d->T > 0 && (!topk_idx || !pair_to_row || !row_to_pair)) return MOE_ERR_INVALID_ARG;
+  if (d->E > 1024) return MOE_ERR_UNSUPPORTED;
+  const int32_t n_pairs = d->T * d->top_k;
+  // the chunk histograms must fit the static array; nothing is allocated when they do not
+  if (moe::layout_ws_bytes(n_pairs, d->E) > MOE_LAYOUT_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  int32_t* scratch = nullptr;
+  if (moe::layout_noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+  // every histogram entry a kernel reads is written earlier in the same call: nothing to clear
+  moe::LayoutArgs a{topk_idx, expert_counts, expert_offsets, rank_counts, rank_offsets, pair_to_row, row_to_pair,
+                    scratch, n_pairs, d->E, d->ep_size, capacity_of(d)};
+  return hip_status(moe::launch_layout(a, stream));
+}
+
 int moe_permute(const moe_dims* d, const void* x, const int32_t* pair_to_row, void* x_perm, hipStream_t stream) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;

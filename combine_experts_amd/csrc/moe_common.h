@@ -50,6 +50,8 @@ struct LayoutArgs {
 constexpr int kLayoutChunk = 512;  // pairs per wave-sized chunk of the stable layout
 size_t layout_ws_bytes(int32_t n_pairs, int32_t E);
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t s);
+// device address of this GPU's static layout scratch (MOE_LAYOUT_NOALLOC_SCRATCH_BYTES)
+hipError_t layout_noalloc_scratch(int32_t** out);
 
 struct RouteArgs {
   const void* x;

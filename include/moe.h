@@ -164,6 +164,19 @@ int moe_dispatch_layout(const moe_dims* d, const int32_t* topk_idx, int32_t* exp
                         int32_t* pair_to_row, int32_t* row_to_pair, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* moe_dispatch_layout for callers that cannot allocate (code under HIP graph capture, serving loops
+ * or harnesses that forbid hipMalloc): the same outputs, bit for bit, with no workspace argument.
+ * Its per-chunk histograms live in a static device array of the library, MOE_LAYOUT_NOALLOC_SCRATCH_BYTES
+ * (1 MiB) per GPU, held until the process ends; nothing is allocated, freed or cleared per call.
+ * Limit: ceil(T*top_k / 512) * E * 4 bytes must fit that array (e.g. T*top_k = 131072 pairs over up
+ * to E = 1024 experts); larger problems return MOE_ERR_WORKSPACE before anything is enqueued.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU (different streams,
+ * or threads without ordering) race and must be serialised by the caller. */
+#define MOE_LAYOUT_NOALLOC_SCRATCH_BYTES (1u << 20)
+int moe_dispatch_layout_noalloc(const moe_dims* d, const int32_t* topk_idx, int32_t* expert_counts,
+                                int32_t* expert_offsets, int32_t* rank_counts, int32_t* rank_offsets,
+                                int32_t* pair_to_row, int32_t* row_to_pair, hipStream_t stream);
+
 /* Permute ([EPLLM] pipeline step 2): x_perm[pair_to_row[t*k+j]] = x[t] for every kept pair.
  *   x [T,D] dtype in; pair_to_row [T*top_k] int32 in; x_perm [T*top_k, D] dtype out (rows >= N are
  *   left untouched). A bit-exact copy; each x row is read once. */

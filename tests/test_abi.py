@@ -116,6 +116,20 @@ def test_unsupported_shapes_reported():
         M.MOE_ERR_UNSUPPORTED
 
 
+def test_noalloc_layout_limit_checked_on_host():
+    # the allocation-free layout refuses, before any GPU call, a problem whose chunk histograms
+    # (ceil(T*k/512) * E int32) exceed its static 1 MiB array
+    lib = M.load_library()
+    fake = 0x1000
+    assert M.MOE_LAYOUT_NOALLOC_SCRATCH_BYTES == 1 << 20
+    d = M.make_dims(16384 + 64, 64, 1024, 8, 64, ep_size=8)     # 257 chunks x 1024 experts x 4 B > 1 MiB
+    assert lib.moe_dispatch_layout_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_WORKSPACE
+    d = M.make_dims(16, 64, 8, 2, 64)
+    assert lib.moe_dispatch_layout_noalloc(ctypes.byref(d), None, fake, fake, fake, fake, fake, fake, None) == \
+        M.MOE_ERR_INVALID_ARG
+
+
 def test_workspace_checks():
     lib = M.load_library()
     fake = 0x1000
