@@ -19,9 +19,12 @@
 // last tile exit, so the host never reads counts. The bf16 path is described above its kernel;
 // the float32 path (small workloads only) is a plain LDS-tiled FMA GEMM on a 2-D grid.
 #include "moe_common.h"
+#include "gemm_geometry.h"
 
 namespace moe {
 namespace {
+
+using namespace geom;
 
 // Block-wide exclusive scan (256 threads); returns the exclusive prefix, sets *total.
 __device__ __forceinline__ int block_scan_256(int v, int* lds4, int* total) {
@@ -108,14 +111,7 @@ __device__ __forceinline__ float act_silu_fast(float a) { return a * __builtin_a
 // row-tile-major inside a group. Rows past the expert's count are loaded from row 0 (finite
 // values) and never stored; 32-row blocks entirely past the count are not multiplied.
 // ---------------------------------------------------------------------------------------------------
-constexpr int GW = 8, GTH = GW * MOE_WAVE;        // waves / threads per block
-constexpr int GBM = 320, GBR = 256, GBK = 64;      // tile rows, B rows per tile, K per stage
-constexpr int GMB = GBM / 64;                       // 32-row blocks per wave (two wave rows)
-constexpr int GKCH = GBK / 8;                       // 16-byte chunks per tile row
-constexpr int G_ACH = GBM * GKCH, G_STAGE = (GBM + GBR) * GKCH, G_LPS = G_STAGE / GTH, G_KS = GBK / 16;
-constexpr int G_GN = 4;                             // column tiles per group in the tile order
-
-__device__ __forceinline__ int gswz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
+static_assert(kLanes == MOE_WAVE, "the GEMM geometry assumes 64-wide wavefronts");
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -232,7 +228,6 @@ __device__ __forceinline__ int gbrow(int wn, int j) {
   else return wn * 64 + j * 32;
 }
 
-constexpr int G_NAL = G_ACH / GTH;  // A loads per stage and lane
 
 // B stored K-major per expert ([K][N], N contiguous: the weights as the forward keeps them, read by
 // the data-gradient GEMMs). A stage's B slice is 64 rows of 256 columns (512 bytes each) in LDS, the
@@ -301,16 +296,16 @@ __device__ __forceinline__ void gemm_kloop(f32x16 (&acc)[GMB][2], bf16x8* lds0, 
   // loads from b0, the rest from b1); A loads wholly past the tile's rows are skipped (those rows
   // feed only accumulators that are never stored)
   auto issue = [&](int kt, bf16x8* slot, int i) {
-    if (i < G_NAL && i * (GTH / GKCH) >= mrows) return;
+    if (i < G_NAL && a_load_skipped(i, mrows)) return;
     bf16x8* dst = slot + i * GTH + wave * MOE_WAVE;
     if (i < G_NAL) {
-      dma16(ds.a, ds.off[i], (uint32_t)kt * (GBK * 2), dst);
+      dma16(ds.a, ds.off[i], stage_soff(kt), dst);
     } else if constexpr (BT) {
       const int k0 = kt * GBK;
       const bool lo = k0 < bt.ksplit;
       dma16(lo ? ds.b0 : ds.b1, ds.off[i], (uint32_t)(lo ? k0 : k0 - bt.ksplit) * (uint32_t)bt.nout * 2u, dst);
     } else {
-      dma16(i < G_NAL + (G_LPS - G_NAL) / 2 ? ds.b0 : ds.b1, ds.off[i], (uint32_t)kt * (GBK * 2), dst);
+      dma16(b_load_second(i) ? ds.b1 : ds.b0, ds.off[i], stage_soff(kt), dst);
     }
   };
   bf16x8 fa[2][GMB], fb[2][2];
@@ -436,11 +431,11 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   ds.a = dma_rsrc(gather ? A : A + (size_t)row0 * K);
 #pragma unroll
   for (int i = 0; i < G_NAL; ++i) {
-    const int slot = i * GTH + wave * MOE_WAVE + lane;
-    const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
+    int row, ch;
+    a_load_pos(i, wave, lane, &row, &ch);
     const int r = row < mrows ? row : 0;
     const uint32_t arow = gather ? (uint32_t)(gather[row0 + r] / gdiv) : (uint32_t)r;
-    ds.off[i] = arow * (uint32_t)K * 2u + ch * 16;
+    ds.off[i] = a_load_off(arow, K, ch);
   }
   const FragIdx fi = frag_idx<DUAL>(lane, wm, wn);
   BtSrc bt{};
@@ -449,12 +444,11 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     ds.b1 = DUAL ? dma_rsrc(B1 + ((size_t)e * Nout + n0) * K) : ds.b0;
 #pragma unroll
     for (int i = G_NAL; i < G_LPS; ++i) {
-      const int bs = i * GTH + wave * MOE_WAVE + lane - G_ACH;
-      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
+      int row, ch;
+      b_load_pos(i, wave, lane, &row, &ch);
       // the paired tile's second half (W3 rows) sits in the second half of the B loads; rows past
       // Nout re-read the slice's first row (never stored)
-      const int f = DUAL ? row % (GBR / 2) : row;
-      ds.off[i] = (n0 + f < Nout ? (uint32_t)f * (uint32_t)K * 2u : 0u) + ch * 16;
+      ds.off[i] = b_load_off(b_weight_row(row, DUAL), n0, Nout, K, ch);
     }
   } else {
     ds.b0 = dma_rsrc(B0 + (size_t)e * ksplit * Nout + n0);
@@ -463,9 +457,9 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     bt.nout = Nout;
 #pragma unroll
     for (int i = G_NAL; i < G_LPS; ++i) {
-      const int bs = i * GTH + wave * MOE_WAVE + lane - G_ACH;  // chunk of the B region this lane fills
-      const int k = bs / (GBR / 8), c = (bs % (GBR / 8)) ^ ((k & 3) << 2);
-      ds.off[i] = (uint32_t)(k * Nout + (n0 + c * 8 < Nout ? c * 8 : 0)) * 2u;  // columns past Nout: never stored
+      int k, c;
+      bt_load_pos(i, wave, lane, &k, &c);     // chunk of the B region this lane fills
+      ds.off[i] = bt_load_off(k, c, n0, Nout);  // columns past Nout: never stored
     }
     const int g = lane / 16, e4 = (lane % 16) / 4, q = lane % 4;
 #pragma unroll
@@ -639,13 +633,12 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
   ds.b1 = ds.b0;
 #pragma unroll
   for (int i = 0; i < G_LPS; ++i) {
-    const int slot = i * GTH + wave * MOE_WAVE + lane;
-    if (i * GTH < G_ACH) {
-      const int row = slot / GKCH, ch = gswz(row, slot % GKCH);
+    int row, ch;
+    if (i < G_NAL) {
+      a_load_pos(i, wave, lane, &row, &ch);
       ds.off[i] = (uint32_t)((row < mrows ? row : 0) * ld) * 2u + ch * 16;
     } else {
-      const int bs = slot - G_ACH;
-      const int row = bs / GKCH, ch = gswz(row, bs % GKCH);
+      b_load_pos(i, wave, lane, &row, &ch);
       ds.off[i] = (uint32_t)((n0 + row < N ? row : 0) * ld) * 2u + ch * 16;
     }
   }

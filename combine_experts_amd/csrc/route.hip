@@ -20,6 +20,7 @@
 #include <atomic>
 
 #include "moe_common.h"
+#include "route_geometry.h"
 
 namespace moe {
 namespace {
@@ -51,9 +52,11 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "me
 // padded to a whole number of chunks per thread so every thread issues the same number of loads.
 template <int NT>
 struct RouteStage {
-  static constexpr int XCH = kTokPerBlock * (kKC / 8);
-  static constexpr int CH = XCH + NT * 16 * (kKC / 8);
-  static constexpr int LPT = (CH + kThreads - 1) / kThreads;  // direct loads per thread per stage
+  static_assert(rgeom::kTokPerBlock == kTokPerBlock && rgeom::kThreads == kThreads && rgeom::kKC == kKC,
+                "router geometry");
+  static constexpr int XCH = rgeom::stage_xch();
+  static constexpr int CH = rgeom::stage_ch(NT);
+  static constexpr int LPT = rgeom::stage_lpt(NT);  // direct loads per thread per stage
   static constexpr int PCH = LPT * kThreads;                   // padded chunks per stage
   static constexpr int DEPTH = NT >= 16 ? 4 : 6;               // ring slots
   static constexpr size_t BYTES = (size_t)DEPTH * PCH * 16;
@@ -82,16 +85,9 @@ __device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ x, const 
   const bf16_t* src[S::LPT];
 #pragma unroll
   for (int i = 0; i < S::LPT; ++i) {
-    const int slot = i * kThreads + tid;
-    if (slot < S::XCH) {
-      const int row = slot / (kKC / 8), ch = swz(row, slot % (kKC / 8));
-      const int tok = t0 + row;
-      src[i] = x + (size_t)(tok < T ? tok : T - 1) * D + ch * 8;  // rows past T: values unused
-    } else {
-      const int ws = slot < S::CH ? slot - S::XCH : 0;  // padding slots reload chunk 0 of row 0
-      const int row = ws / (kKC / 8), ch = swz(row, ws % (kKC / 8));
-      src[i] = wg + (size_t)(row < E ? row : E - 1) * D + ch * 8;  // padded experts reuse a real row
-    }
+    bool from_x;
+    const size_t off = rgeom::load_src(NT, i, tid, t0, T, D, E, &from_x);
+    src[i] = (from_x ? x : wg) + off;
   }
   auto issue = [&](int kc, int slot) {
 #pragma unroll
