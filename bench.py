@@ -33,7 +33,6 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 STAGES = ["route", "layout", "ffn_up", "ffn_down", "combine"]   # ffn_up includes the permute
 DOMINANT = "ffn_up"
 DOMINANT_SRC = os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip")
-CPU_SAMPLE_TOKENS = {"tiny_fp32": 256, "switch_cap": 2048, "mixtral": 64, "dsv3": 40, "skew": 256}
 
 
 def log(*a):
@@ -64,33 +63,93 @@ def read_traffic(workload: str):
         return None
 
 
-def cpu_baseline(cfg, inp, n_tokens: int):
-    """The CPU oracle, untouched, on the first n_tokens tokens of the same workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, n_random_rows: int = 512, seed: int = 0):
+    """The CPU oracle, untouched, timed on the host cores: route, dispatch layout, permute and combine on
+    all T tokens; the expert FFN on a seeded sample of rows (the first and last row of every non-empty
+    expert group, n_random_rows random rows, and at the skewed workload all rows of the hottest expert),
+    extrapolated to all N kept rows. The oracle's FFN costs a fixed amount per expert (its weights are
+    upcast to float64 once) plus a cost per row, so the estimate is the sample's time plus the rows not
+    in the sample at the marginal cost of a row, measured on the busiest expert (its FFN over all its
+    rows against over two of them). The combine reads an x_perm-shaped stand-in for the expert outputs
+    (its cost does not depend on their values)."""
     import numpy as np
     import threadpoolctl
     import oracle as O
 
-    S = min(n_tokens, cfg.T)
-    x = inp["x"][:S].cpu()
+    T, k = cfg.T, cfg.top_k
+    x = inp["x"].cpu()
     wg = inp["w_gate"].cpu()
     bias = None if inp["bias"] is None else inp["bias"].cpu()
-    # which experts the sample reaches (so their weights are in host memory before timing)
-    r0 = O.route(x, wg, bias, cfg.top_k, cfg.gate, cfg.n_groups, cfg.topk_groups)
-    experts = sorted(set(np.asarray(r0["topk_idx"]).reshape(-1).tolist()))
-    host_w = {key: ({e: inp[key][e].cpu() for e in experts} if inp[key] is not None else None)
-              for key in ("w1", "w3", "w2")}
-    threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) if threadpoolctl.threadpool_info() else 1
+    # every expert's weights in host memory (bf16 or f32 as stored) before timing
+    host_w = {key: (None if inp[key] is None else inp[key].cpu()) for key in ("w1", "w3", "w2")}
+    info = threadpoolctl.threadpool_info()
+    threads = max((i.get("num_threads", 1) for i in info), default=1)
+    t = {}
     t0 = time.perf_counter()
-    r = O.route(x, wg, bias, cfg.top_k, cfg.gate, cfg.n_groups, cfg.topk_groups)
-    C = O.capacity(cfg.capacity_factor, S, cfg.top_k, cfg.E)
+    r = O.route(x, wg, bias, k, cfg.gate, cfg.n_groups, cfg.topk_groups)
+    t["route"] = time.perf_counter() - t0
+    C = O.capacity(cfg.capacity_factor, T, k, cfg.E)
+    t0 = time.perf_counter()
     lay = O.dispatch_layout(r["topk_idx"], cfg.E, cfg.ep_size, C)
-    xp = O.permute(O.as_f64(x), lay["row_to_pair"], cfg.top_k, lay["n_kept"])
-    yp = O.expert_ffn(xp, lay["expert_offsets"], host_w["w1"], host_w["w3"], host_w["w2"], cfg.act)
-    O.combine(yp, lay["pair_to_row"], r["topk_gate"], S, cfg.top_k)
-    dt = time.perf_counter() - t0
-    return {"value": S / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {S} of {cfg.T} tokens ({S * cfg.top_k} pairs, {len(experts)} experts' weights "
-                      f"in host memory), whole layer in float64, {dt:.1f} s"}
+    t["layout"] = time.perf_counter() - t0
+    N = lay["n_kept"]
+    t0 = time.perf_counter()
+    xp = O.permute(O.as_f64(x), lay["row_to_pair"], k, N)
+    t["permute"] = time.perf_counter() - t0
+    # FFN sample
+    off = lay["expert_offsets"]
+    rng = np.random.default_rng(seed)
+    rows = set()
+    nonempty = [e for e in range(cfg.E) if off[e + 1] > off[e]]
+    for e in nonempty:
+        rows |= {int(off[e]), int(off[e + 1] - 1)}
+    if N > 0:
+        rows |= set(rng.choice(N, size=min(n_random_rows, N), replace=False).tolist())
+    if cfg.name == "skew" and nonempty:
+        hot = max(nonempty, key=lambda e: off[e + 1] - off[e])
+        rows |= set(range(int(off[hot]), int(off[hot + 1])))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    experts = np.searchsorted(off, rows, side="right") - 1
+    t0 = time.perf_counter()
+    O.expert_ffn_rows(xp[rows], experts, host_w["w1"], host_w["w3"], host_w["w2"], cfg.act)
+    t_ffn_sample = time.perf_counter() - t0
+    per_row, busiest = 0.0, -1
+    if nonempty:
+        busiest = max(nonempty, key=lambda e: off[e + 1] - off[e])
+        lo, hi = int(off[busiest]), int(off[busiest + 1])
+        one = np.full(hi - lo, busiest)
+        t0 = time.perf_counter()
+        O.expert_ffn_rows(xp[lo:lo + 2], one[:2], host_w["w1"], host_w["w3"], host_w["w2"], cfg.act)
+        t_two = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.expert_ffn_rows(xp[lo:hi], one, host_w["w1"], host_w["w3"], host_w["w2"], cfg.act)
+        t_all = time.perf_counter() - t0
+        per_row = max(t_all - t_two, 0.0) / max(hi - lo - 2, 1)
+    t["ffn"] = t_ffn_sample + max(N - len(rows), 0) * per_row
+    t0 = time.perf_counter()
+    O.combine(xp, lay["pair_to_row"], r["topk_gate"], T, k)
+    t["combine"] = time.perf_counter() - t0
+    total = sum(t.values())
+    return {"value": round(T / total, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+            "stage_s": {s_: round(v, 3) for s_, v in t.items()},
+            "sample": f"route, layout, permute and combine on all {T} tokens ({N} kept rows); the expert FFN "
+                      f"on {len(rows)} of {N} rows (first and last row of each of {len(nonempty)} non-empty "
+                      f"experts, {min(n_random_rows, N)} random rows" + (", all rows of the hottest expert"
+                                                                        if cfg.name == "skew" else "") +
+                      f") in {t_ffn_sample:.1f} s, plus the other {max(N - len(rows), 0)} rows at "
+                      f"{per_row * 1e3:.3f} ms each, the marginal row cost on expert {busiest} ('sampled'); "
+                      f"float64; {threads} BLAS threads on {os.cpu_count()} logical CPUs"}
 
 
 def measure_cluster(M, W, torch, cfg, d, inp, buf, stream, time_calls, b):
@@ -283,7 +342,8 @@ def main(argv=None):
     ap.add_argument("--no-extras", action="store_true",
                     help="time only the forward step (no load-balancing, cluster, padded, executor or backward "
                          "measurements), e.g. under a profiler")
-    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--cpu-random-rows", type=int, default=512,
+                    help="random rows in the CPU oracle's expert-FFN sample (besides each expert's first and last)")
     ap.add_argument("--copy-calib-bytes", type=int, default=0,
                     help="before the timed steps, copy a buffer of this many bytes 3 times (a plain copy kernel "
                          "of known size, to scale HBM byte counters)")
@@ -354,15 +414,30 @@ def main(argv=None):
     per_step = {s: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, s in enumerate(STAGES)}
     stage_med = {s: v[len(v) // 2] for s, v in per_step.items()}
     stage_min = {s: v[0] for s, v in per_step.items()}
-    # the standalone permute kernel (outside the timed steps), for its bandwidth
+    # the standalone permute kernel (outside the timed steps), for its bandwidth: each timed call starts
+    # from a cold cache (a 768 MiB copy, three times the 256 MiB Infinity Cache, runs before it), so
+    # neither x nor x_perm is served from a cache a previous repetition filled; the back-to-back figure
+    # (same buffers, warm) is reported beside it
     M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+    flush_src = torch.empty(384 << 20, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    cold = []
+    for _ in range(10):
+        flush_dst.copy_(flush_src)
+        ca, cz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ca.record(stream)
+        M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
+        cz.record(stream)
+        cold.append((ca, cz))
     pa, pz = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     pa.record(stream)
     for _ in range(20):
         M.moe_permute(d, inp["x"], buf.pair_to_row, buf.x_perm, stream)
     pz.record(stream)
     torch.cuda.synchronize()
-    permute_ms = pa.elapsed_time(pz) / 20
+    permute_ms = sum(a.elapsed_time(z) for a, z in cold) / len(cold)
+    permute_warm_ms = pa.elapsed_time(pz) / 20
+    del flush_src, flush_dst
     # the same step captured once in a HIP graph and replayed (one launch per step)
     gl = M.GraphLayer(d, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], device=dev)
     for _ in range(args.warmup):
@@ -389,6 +464,7 @@ def main(argv=None):
     permute_bytes = cfg.T * cfg.D * b + N * cfg.D * b + cfg.T * cfg.top_k * 4
     combine_bytes = N * cfg.D * b + cfg.T * cfg.D * b + cfg.T * cfg.top_k * 8
     permute_gbs = permute_bytes / (permute_ms * 1e-3) / 1e9
+    permute_warm_gbs = permute_bytes / (permute_warm_ms * 1e-3) / 1e9
     combine_gbs = combine_bytes / (stage_ms["combine"] * 1e-3) / 1e9
     traffic = read_traffic(cfg.name)
     # every stage against its own roofline: algorithmic bytes and flops at the realised N, spec peaks
@@ -419,7 +495,8 @@ def main(argv=None):
     for s in STAGES:
         log(f"[bench]   {s:9s} {stage_ms[s] * 1e3:9.1f} us")
     log(f"[bench] step as a HIP graph replay: {graph_ms * 1e3:.1f} us")
-    log(f"[bench] permute {permute_gbs:.0f} GB/s, combine {combine_gbs:.0f} GB/s, "
+    log(f"[bench] permute {permute_gbs:.0f} GB/s from a cold cache ({permute_warm_gbs:.0f} GB/s back to back), "
+        f"combine {combine_gbs:.0f} GB/s, "
         f"FFN {ffn_tflops:.0f} TFLOP/s ({ffn_tflops / peak * 100:.1f}% of peak)")
 
     extra_ms, cluster, padded, overlap, bwd = {}, None, None, None, None
@@ -475,10 +552,10 @@ def main(argv=None):
 
     cpu = None
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or CPU_SAMPLE_TOKENS.get(cfg.name, 8)
-        log(f"[bench] CPU oracle baseline on {n} tokens ...")
-        cpu = cpu_baseline(cfg, inp, n)
-        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s ({cpu['sample']})")
+        log("[bench] CPU oracle baseline ...")
+        cpu = cpu_baseline(cfg, inp, args.cpu_random_rows)
+        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s, stages {cpu['stage_s']} s ({cpu['sample']}; "
+            f"{cpu['cpu_model']})")
 
     out = {
         "metric": METRIC, "value": round(cfg.T / (ms_per_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -498,12 +575,14 @@ def main(argv=None):
         "permute": "inside ffn_up (rows gathered from x by the GEMM's loads)",
         "graph": {"ms_per_step": round(graph_ms, 4), "tokens_per_s": round(cfg.T / (graph_ms * 1e-3), 1),
                   "note": "the same step captured once in a HIP graph and replayed"},
-        "extra_stage_ms": {"permute_standalone": round(permute_ms, 4), **{s: round(v, 4) for s, v in extra_ms.items()}},
+        "extra_stage_ms": {"permute_standalone": round(permute_ms, 4), "permute_standalone_warm": round(permute_warm_ms, 4),
+                           **{s: round(v, 4) for s, v in extra_ms.items()}},
         "cluster_emulation": cluster,
         "padded_capacity": padded,
         "overlap": overlap,
         "backward": bwd,
-        "permute_gbps": round(permute_gbs, 1), "combine_gbps": round(combine_gbs, 1),
+        "permute_gbps": round(permute_gbs, 1), "permute_gbps_warm": round(permute_warm_gbs, 1),
+        "combine_gbps": round(combine_gbs, 1),
         "gemm_mfma_frac": round(ffn_tflops / peak, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
