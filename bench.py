@@ -384,7 +384,7 @@ def main(argv=None):
                                    stream)
         if ev is not None:
             ev[3].record(stream)
-        M.moe_expert_ffn_down(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm, stream)
+        M.moe_expert_ffn_down_splitk(d, buf.h, buf.expert_offsets, inp["w2"], buf.y_perm, buf.down_ws, stream)
         if ev is not None:
             ev[4].record(stream)
         M.moe_unpermute_combine(d, buf.y_perm, buf.pair_to_row, buf.topk_gate, buf.y, stream)

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     moe_expert_ffn_up_backward, moe_expert_ffn_down_backward_w, moe_expert_ffn_up_backward_w, moe_router_backward, moe_backward_dx, moe_wgrad_ld, moe_group_transpose,
     moe_expert_wgrad, MOE_STAGE_ROUTER_BWD, moe_layer_backward, moe_backward_args,
     moe_permute, moe_expert_ffn, moe_expert_ffn_up, moe_expert_ffn_up_gather, moe_expert_ffn_down,
+    moe_expert_ffn_down_splitk, MOE_STAGE_FFN_DOWN,
     moe_unpermute_combine,
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL, MOE_ACT_SWIGLU, MOE_ACT_GELU,

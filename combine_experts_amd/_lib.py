@@ -20,7 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 MOE_GATE_SOFTMAX_TOPK, MOE_GATE_SIGMOID_TOPK, MOE_GATE_SOFTMAX_FULL = 0, 1, 2
 MOE_ACT_SWIGLU, MOE_ACT_GELU = 0, 1
 MOE_F32, MOE_BF16 = 0, 1
-MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS, MOE_STAGE_ROUTER_BWD = 0, 1, 2, 3
+MOE_STAGE_LAYOUT, MOE_STAGE_FFN, MOE_STAGE_ROUTE_STATS, MOE_STAGE_ROUTER_BWD, MOE_STAGE_FFN_DOWN = 0, 1, 2, 3, 4
 
 
 class MoEError(RuntimeError):
@@ -105,6 +105,7 @@ _SIG = {
     "moe_expert_ffn_up": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_up_gather": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, _P, _P]),
     "moe_expert_ffn_down": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
+    "moe_expert_ffn_down_splitk": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_unpermute_combine": (ctypes.c_int, [ctypes.POINTER(moe_dims), _P, _P, _P, _P, _P]),
 }
 
@@ -298,6 +299,18 @@ def moe_expert_ffn_down(d: moe_dims, h, expert_offsets, w2, y_perm, stream=None)
         ctypes.byref(d), _ptr(h, "h", dt, P * d.F), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
         _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_perm, "y_perm", dt, P * d.D), _stream(stream))
     _check("moe_expert_ffn_down", st)
+
+
+def moe_expert_ffn_down_splitk(d: moe_dims, h, expert_offsets, w2, y_perm, ws, stream=None) -> None:
+    """moe_expert_ffn_down with the optional split-K workspace (moe_workspace_size(MOE_STAGE_FFN_DOWN)
+    bytes; None: the plain down-projection)."""
+    dt = _elem_dtype(d)
+    P = d.T * d.top_k
+    st = load_library().moe_expert_ffn_down_splitk(
+        ctypes.byref(d), _ptr(h, "h", dt, P * d.F), _ptr(expert_offsets, "expert_offsets", torch.int32, d.E + 1),
+        _ptr(w2, "w2", dt, d.E * d.D * d.F), _ptr(y_perm, "y_perm", dt, P * d.D), _ptr(ws, "ws", nullable=True),
+        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("moe_expert_ffn_down_splitk", st)
 
 
 def moe_expert_ffn(d: moe_dims, x_perm, expert_offsets, w1, w3, w2, y_perm, ws, stream=None) -> None:

@@ -21,6 +21,8 @@
 #include "moe_common.h"
 #include "gemm_geometry.h"
 
+#include <algorithm>
+
 namespace moe {
 namespace {
 
@@ -142,7 +144,7 @@ __device__ __forceinline__ int block_scan_g(int v, int* lds, int* total) {
 }
 
 // This block's (expert, row tile, column tile), or false when it has none.
-__device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT, int* e_out, int* mt_out,
+__device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT, int blk, int* e_out, int* mt_out,
                              int* nt_out, int* o0_out, int* cnt_out) {
   __shared__ int s_tmp[GW];
   __shared__ int s_e, s_local, s_cnt, s_o0;
@@ -155,7 +157,7 @@ __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT,
     int L;
     const int start = block_scan_g(n, s_tmp, &L);
     const int per = (L + 7) / 8;
-    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int xcd = blk % 8, j = blk / 8;
     if (j >= per) return false;
     const int t = xcd * per + j;
     if (t >= L) return false;
@@ -187,7 +189,7 @@ __device__ bool map_tile_xcd(const int32_t* __restrict__ offsets, int E, int NT,
     L += tot;
   }
   const int per = (L + 7) / 8;
-  const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int xcd = blk % 8, j = blk / 8;
   if (j >= per) return false;
   const int t = xcd * per + j;
   if (t >= L) return false;
@@ -404,20 +406,30 @@ __device__ __forceinline__ float act_gelu_grad(float a) {
 //   EPI_BWD    acc = dh (no activation on the way in); with a1 (and a3) read from pre as EPI_PRE wrote
 //              them: SwiGLU out[r, n] = dh*a3*SiLU'(a1), out[r, Nout + n] = dh*SiLU(a1) (2*Nout wide);
 //              GELU out[r, n] = dh*GELU'(a1) (Nout wide)
-constexpr int EPI_PLAIN = 0, EPI_PRE = 1, EPI_BWD = 2;
+//   EPI_PARTIAL  split K: block (tile, s) sums K stages [s*nk/S, (s+1)*nk/S) and stores the float32 partial
+//              to part[s][row][n] ([S][n_rows_max][Nout]); splitk_reduce_bf16 adds the S partials in
+//              order s = 0 .. S-1 and rounds once
+constexpr int EPI_PLAIN = 0, EPI_PRE = 1, EPI_BWD = 2, EPI_PARTIAL = 3;
 
 template <int ACTFN, bool DUAL, int EPI = EPI_PLAIN, bool BT = false>
 __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ A, const int32_t* __restrict__ offsets,
                                                      const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1,
                                                      bf16_t* __restrict__ out, int E, int K, int Nout,
                                                      bf16_t* __restrict__ pre, const int32_t* __restrict__ gather,
-                                                     int gdiv, int ksplit) {
+                                                     int gdiv, int ksplit, int splits, float* __restrict__ part,
+                                                     int n_rows_max) {
   static_assert(!(BT && DUAL), "the K-major B form has no paired W1/W3 tile");
+  static_assert(EPI != EPI_PARTIAL || (!BT && !DUAL && ACTFN < 0), "split K: plain down-projection tile only");
   constexpr int BNO = DUAL ? GBR / 2 : GBR;  // output columns per tile
   __shared__ bf16x8 lds0[G_STAGE], lds1[G_STAGE];  // the two slots of the K ring
   const int NT = (Nout + BNO - 1) / BNO;
+  // split K: the S blocks of a tile are adjacent; block (tile, s) takes stages [s*nk/S, (s+1)*nk/S)
+  const int split = EPI == EPI_PARTIAL ? (int)(blockIdx.x % splits) : 0;
+  const int blk = EPI == EPI_PARTIAL ? (int)(blockIdx.x / splits) : (int)blockIdx.x;
+  const int kt0 = EPI == EPI_PARTIAL ? split * (K / GBK) / splits : 0;
+  const int kt1 = EPI == EPI_PARTIAL ? (split + 1) * (K / GBK) / splits : K / GBK;
   int e, mt, nt, o0, cnt;
-  if (!map_tile_xcd(offsets, E, NT, &e, &mt, &nt, &o0, &cnt)) return;
+  if (!map_tile_xcd(offsets, E, NT, blk, &e, &mt, &nt, &o0, &cnt)) return;
   const int row0 = o0 + mt * GBM;
   const int mrows = min(GBM, cnt - mt * GBM);
   const int n0 = nt * BNO;
@@ -428,7 +440,8 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   // row tile's base, or from x itself (gathered rows: byte offsets from x, which the host keeps under
   // 4 GiB); the weights from the tile's first weight row
   DmaSrc ds;
-  ds.a = dma_rsrc(gather ? A : A + (size_t)row0 * K);
+  const int k0 = kt0 * GBK;  // first K column of this block's stages (split K), else 0
+  ds.a = dma_rsrc((gather ? A : A + (size_t)row0 * K) + k0);
 #pragma unroll
   for (int i = 0; i < G_NAL; ++i) {
     int row, ch;
@@ -440,8 +453,8 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   const FragIdx fi = frag_idx<DUAL>(lane, wm, wn);
   BtSrc bt{};
   if constexpr (!BT) {
-    ds.b0 = dma_rsrc(B0 + ((size_t)e * Nout + n0) * K);
-    ds.b1 = DUAL ? dma_rsrc(B1 + ((size_t)e * Nout + n0) * K) : ds.b0;
+    ds.b0 = dma_rsrc(B0 + ((size_t)e * Nout + n0) * K + k0);
+    ds.b1 = DUAL ? dma_rsrc(B1 + ((size_t)e * Nout + n0) * K + k0) : ds.b0;
 #pragma unroll
     for (int i = G_NAL; i < G_LPS; ++i) {
       int row, ch;
@@ -480,7 +493,7 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-  const int nk = K / GBK;
+  const int nk = kt1 - kt0;
   // every wave runs the same stages and barriers; a wave with no rows multiplies one block
   switch (act) {
     case 5: gemm_kloop<5, BT>(acc, lds0, lds1, ds, fi, bt, wave, nk, mrows); break;
@@ -491,6 +504,31 @@ __global__ void __launch_bounds__(GTH) ffn_gemm_bf16(const bf16_t* __restrict__ 
   }
   // acc[i][j][v]: token row (2i+wm)*32 + lane%32, B row gbrow(wn,j) + 8*(v/4) + 4*(lane/32) + v%4
   constexpr bool SWI = ACTFN == MOE_ACT_SWIGLU;
+  if constexpr (EPI == EPI_PARTIAL) {
+    // float32 tile out through LDS, as the weight-gradient tiles: each wave stages its 32-row blocks
+    // (32 x 64 floats) in the ring slot the last stage did not read and stores 256-byte row pieces
+    constexpr int SROW = 64 + 4;
+    float* stg = reinterpret_cast<float*>((nk & 1) ? lds1 : lds0) + wave * 32 * SROW;
+    float* pbase = part + (size_t)split * n_rows_max * Nout;
+#pragma unroll
+    for (int i = 0; i < GMB; ++i) {
+      if (i >= act) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4*>(stg + (lane % 32) * SROW + j * 32 + 8 * q + 4 * (lane / 32)) =
+              f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += MOE_WAVE / 16) {
+        const int r2 = rr + lane / 16, c2 = (lane % 16) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(stg + r2 * SROW + c2);
+        const int r = (2 * i + wm) * 32 + r2, c = n0 + wn * 64 + c2;
+        if (r < mrows && c < Nout) *reinterpret_cast<f32x4*>(pbase + (size_t)(row0 + r) * Nout + c) = v;
+      }
+    }
+    return;
+  }
   if constexpr (EPI == EPI_PLAIN) {
     // through LDS: each wave stages its 32-row blocks in the ring slot the last stage did not read
     // (every wave passed the barrier after its last read of it) and stores whole 16-byte row pieces,
@@ -676,6 +714,23 @@ __global__ void __launch_bounds__(GTH) ffn_wgrad_bf16(const bf16_t* __restrict__
   }
 }
 
+// Split-K reduction: out[r, n] = bf16(part[0][r][n] + part[1][r][n] + ... + part[S-1][r][n]), the partials
+// added in that order in float32, for the N = offsets[E] kept rows; 4 columns per thread.
+__global__ void __launch_bounds__(256) splitk_reduce_bf16(const float* __restrict__ part, int splits,
+                                                          const int32_t* __restrict__ offsets, int E,
+                                                          int n_rows_max, int Nout, bf16_t* __restrict__ out) {
+  const int N = offsets[E];
+  const size_t n4 = (size_t)N * Nout / 4, plane = (size_t)n_rows_max * Nout;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(part + i * 4);
+    for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const f32x4*>(part + s * plane + i * 4);
+    bf16x4 o;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = f2bf(v[u]);
+    __builtin_nontemporal_store(o, reinterpret_cast<bf16x4*>(out) + i);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------------
 // float32 grouped GEMM (plain FMA): 64 x 64 tiles, BK = 16, each thread 4 x 4 outputs per B matrix.
 // ---------------------------------------------------------------------------------------------------
@@ -774,10 +829,26 @@ hipError_t launch_ffn_bf16(const FfnArgs& a, hipStream_t s) {
   bf16_t* pr = (bf16_t*)a.pre;
 #define MOE_FFN_LAUNCH(ACTV, DUALV, EPIV)                                                                          \
   hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, DUALV, EPIV>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, a.E, \
-                     a.K, a.Nout, pr, a.gather, a.gather_div, 0)
+                     a.K, a.Nout, pr, a.gather, a.gather_div, 0, 1, nullptr, a.n_rows_max)
 #define MOE_FFN_LAUNCH_BT(ACTV, EPIV)                                                                              \
   hipLaunchKernelGGL((ffn_gemm_bf16<ACTV, false, EPIV, true>), grid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1, o, \
-                     a.E, a.K, a.Nout, pr, a.gather, a.gather_div, a.ksplit > 0 ? a.ksplit : a.K)
+                     a.E, a.K, a.Nout, pr, a.gather, a.gather_div, a.ksplit > 0 ? a.ksplit : a.K, 1, nullptr,      \
+                     a.n_rows_max)
+  if (a.splits > 1) {
+    // split K (plain down-projection only): S blocks per tile write float32 partials, then one pass adds
+    // them in split order and rounds
+    if (a.act >= 0 || a.epi != 0 || a.bt || a.gather || a.part == nullptr || a.K % GBK != 0 ||
+        a.splits > a.K / GBK || a.Nout % 4 != 0)
+      return hipErrorInvalidValue;
+    const dim3 sgrid((unsigned)(grid.x * (unsigned)a.splits));
+    hipLaunchKernelGGL((ffn_gemm_bf16<-1, false, EPI_PARTIAL>), sgrid, dim3(GTH), 0, s, A, a.expert_offsets, b0, b1,
+                       o, a.E, a.K, a.Nout, pr, a.gather, a.gather_div, 0, a.splits, a.part, a.n_rows_max);
+    const long long n4 = (long long)a.n_rows_max * a.Nout / 4;
+    const unsigned rgrid = (unsigned)std::min<long long>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(splitk_reduce_bf16, dim3(rgrid), dim3(256), 0, s, a.part, a.splits, a.expert_offsets, a.E,
+                       a.n_rows_max, a.Nout, o);
+    return hipGetLastError();
+  }
   if (a.bt) {
     if (a.K % GBK != 0 || (a.ksplit > 0 && (a.ksplit % GBK != 0 || a.ksplit > a.K || (a.ksplit < a.K && !b1))))
       return hipErrorInvalidValue;

@@ -3,7 +3,10 @@
 #include <cmath>
 #include <cstdint>
 
+#include <algorithm>
+
 #include "moe_common.h"
+#include "gemm_geometry.h"
 
 namespace {
 
@@ -43,9 +46,33 @@ int32_t capacity_of(const moe_dims* d) {
   return (int32_t)c;
 }
 
+// Splits of the down-projection's reduction: only when the tiles it can have (at most ceil(N_max/GBM)
+// + E row tiles, and at most ceil(C/GBM) per expert) times ceil(D/GBR) column tiles fill at most a
+// quarter of the 256 compute units and F is long enough to split (F/64 >= 32 stages); then as many
+// as keep <= 2 blocks per compute unit and >= 16 stages per block.
+int down_splits(const moe_dims* d) {
+  if (d->dtype != MOE_BF16 || d->T == 0) return 1;
+  const int64_t P = (int64_t)d->T * d->top_k, C = capacity_of(d), bm = moe::geom::GBM;
+  const int64_t mt = std::min<int64_t>((P + bm - 1) / bm + std::min<int64_t>(d->E, P),
+                                       (int64_t)d->E * ((C + bm - 1) / bm));
+  const int64_t tiles = mt * ((d->D + moe::geom::GBR - 1) / moe::geom::GBR);
+  const int nk = d->F / moe::geom::GBK;
+  constexpr int64_t kCUs = 256;
+  if (tiles > kCUs / 4 || nk < 32 || d->F % moe::geom::GBK != 0) return 1;
+  int s = 1;
+  while (s < 8 && tiles * s * 2 <= 2 * kCUs && nk / (s * 2) >= 16) s *= 2;
+  return s;
+}
+
+size_t down_split_ws_bytes(const moe_dims* d) {
+  const int s = down_splits(d);
+  if (s <= 1) return 0;
+  return ((size_t)s * d->T * d->top_k * d->D * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t ffn_ws_bytes(const moe_dims* d) {
   const size_t n_max = (size_t)d->T * d->top_k;
-  return (n_max * d->F * elem_bytes(d) + 255) / 256 * 256;
+  return (n_max * d->F * elem_bytes(d) + 255) / 256 * 256 + down_split_ws_bytes(d);
 }
 
 int row_vec_ok(const moe_dims* d, int n) { return (n * elem_bytes(d)) % 16 == 0; }
@@ -101,6 +128,8 @@ int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes) {
     *bytes = route_partial_rows(d) * (size_t)d->E * sizeof(float);
   } else if (stage == MOE_STAGE_ROUTER_BWD) {
     *bytes = moe::colsum_ws_bytes(d->T, d->E);
+  } else if (stage == MOE_STAGE_FFN_DOWN) {
+    *bytes = down_split_ws_bytes(d);
   } else {
     return MOE_ERR_INVALID_ARG;
   }
@@ -231,6 +260,23 @@ int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_
   return hip_status(d->dtype == MOE_BF16 ? moe::launch_ffn_bf16(a, stream) : moe::launch_ffn_f32(a, stream));
 }
 
+int moe_expert_ffn_down_splitk(const moe_dims* d, const void* h, const int32_t* expert_offsets, const void* w2,
+                               void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  const int splits = down_splits(d);
+  if (ws == nullptr || splits <= 1) return moe_expert_ffn_down(d, h, expert_offsets, w2, y_perm, stream);
+  if (d->T == 0) return MOE_OK;
+  if (!h || !expert_offsets || !w2 || !y_perm) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(y_perm) || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (!ffn_shape_ok(d)) return MOE_ERR_UNSUPPORTED;
+  if (ws_bytes < down_split_ws_bytes(d)) return MOE_ERR_WORKSPACE;
+  moe::FfnArgs a{h, expert_offsets, w2, nullptr, y_perm, d->T * d->top_k, d->E, d->F, d->D, -1};
+  a.splits = splits;
+  a.part = static_cast<float*>(ws);
+  return hip_status(moe::launch_ffn_bf16(a, stream));
+}
+
 int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_offsets, const void* w1,
                    const void* w3, const void* w2, void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_dims(d);
@@ -239,7 +285,10 @@ int moe_expert_ffn(const moe_dims* d, const void* x_perm, const int32_t* expert_
   if (ws == nullptr || ws_bytes < ffn_ws_bytes(d)) return MOE_ERR_WORKSPACE;
   st = moe_expert_ffn_up(d, x_perm, expert_offsets, w1, w3, ws, stream);
   if (st != MOE_OK) return st;
-  return moe_expert_ffn_down(d, ws, expert_offsets, w2, y_perm, stream);
+  // h first, then the down-projection's split-K scratch (when these dims split)
+  const size_t h_bytes = ffn_ws_bytes(d) - down_split_ws_bytes(d);
+  return moe_expert_ffn_down_splitk(d, ws, expert_offsets, w2, y_perm, static_cast<char*>(ws) + h_bytes,
+                                    ws_bytes - h_bytes, stream);
 }
 
 int moe_unpermute_combine_add(const moe_dims* d, const void* y_perm, const int32_t* pair_to_row,

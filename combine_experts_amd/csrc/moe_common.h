@@ -124,6 +124,10 @@ struct FfnArgs {
   // expert) and the rest from b1 ([K - ksplit][Nout])
   int bt = 0;
   int32_t ksplit = 0;
+  // bf16 down-projection only: split K over `splits` blocks per tile, float32 partials in
+  // part [splits][n_rows_max][Nout], then a fixed-order reduction into out
+  int splits = 1;
+  float* part = nullptr;
 };
 hipError_t launch_wgrad_bf16(const void* aT, const void* bT, const int32_t* koff, int G, int M, int N, long long ld,
                              float* out0, float* out1, int split, hipStream_t s);

@@ -37,6 +37,9 @@ class MoELayerBuffers:
         self.h = torch.empty((P, d.F), dtype=dt, device=device)
         self.y_perm = torch.empty((P, d.D), dtype=dt, device=device)
         self.y = torch.empty((d.T, d.D), dtype=dt, device=device)
+        # split-K scratch of moe_expert_ffn_down_splitk, for dims whose down-projection has too few tiles
+        n = L.moe_workspace_size(d, L.MOE_STAGE_FFN_DOWN)
+        self.down_ws = torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
 
     def as_dict(self) -> Dict[str, Optional[torch.Tensor]]:
         return {k: v for k, v in self.__dict__.items() if isinstance(v, torch.Tensor) or v is None}

@@ -74,7 +74,9 @@ enum moe_stage {
   MOE_STAGE_LAYOUT = 0,     /* scratch of moe_dispatch_layout */
   MOE_STAGE_FFN = 1,        /* scratch of moe_expert_ffn */
   MOE_STAGE_ROUTE_STATS = 2, /* the prob_partials buffer of moe_route_ex / moe_load_balance */
-  MOE_STAGE_ROUTER_BWD = 3   /* scratch of moe_router_backward (column-sum partials of dbias) */
+  MOE_STAGE_ROUTER_BWD = 3,  /* scratch of moe_router_backward (column-sum partials of dbias) */
+  MOE_STAGE_FFN_DOWN = 4     /* split-K scratch of moe_expert_ffn_down_splitk; 0 bytes: these dims are
+                                not split */
 };
 
 /* Problem statement of one layer call ([COMM] volume equation: B*S tokens as T, top-k as K,
@@ -102,7 +104,8 @@ typedef struct moe_dims {
 int moe_capacity(const moe_dims* d, int32_t* capacity);
 
 /* Workspace bytes that `stage` needs (MOE_STAGE_LAYOUT: moe_dispatch_layout; MOE_STAGE_FFN:
- * moe_expert_ffn, which keeps the expert hidden activations h[T*top_k, F] there). Host only. */
+ * moe_expert_ffn, which keeps the expert hidden activations h[T*top_k, F] there, followed by the
+ * MOE_STAGE_FFN_DOWN scratch of its down-projection). Host only. */
 int moe_workspace_size(const moe_dims* d, int stage, size_t* bytes);
 
 /* Router ([EPLLM] "The Execution Pipeline" step 1; layer equation of "The Distributed MoE Dilemma").
@@ -215,6 +218,20 @@ int moe_expert_ffn_up_gather(const moe_dims* d, const void* x, const int32_t* ro
 /* Second half of moe_expert_ffn: y_perm[r] = W2[e] h[r]. h [T*top_k, F] in; y_perm [T*top_k, D] out. */
 int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_offsets,
                         const void* w2, void* y_perm, hipStream_t stream);
+
+/* moe_expert_ffn_down with an optional workspace that lets it split the reduction (K = F) over several
+ * blocks per output tile when the problem has too few tiles to fill the GPU ([EPLLM] "Static Capacity
+ * Factors and Token Dropping": a capacity-bound layer leaves each expert at most C rows, so the
+ * down-projection has E x ceil(C/320) x ceil(D/256) tiles). Block s of a tile sums K stages
+ * [s*F/S/64, (s+1)*F/S/64) into a float32 partial; one more pass adds the S partials in split order
+ * and rounds once, so the result is deterministic (it differs from the unsplit sum by float32
+ * rounding only). bf16 only; S > 1 when F >= 2048 and the layer has at most 64 such tiles.
+ *   ws, ws_bytes  moe_workspace_size(MOE_STAGE_FFN_DOWN) bytes: S x T*top_k x D float32 partials. When
+ *                 that size is 0, or ws is NULL, this is moe_expert_ffn_down.
+ * Other arguments as moe_expert_ffn_down. The layer executor does not split (its micro-batches then give
+ * the same bits as the whole batch). */
+int moe_expert_ffn_down_splitk(const moe_dims* d, const void* h, const int32_t* expert_offsets, const void* w2,
+                               void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Unpermute + combine ([EPLLM] pipeline step 6: restore order, weight each of the k expert
  * outputs by its gate and sum; the residual is left to the caller):

@@ -83,14 +83,16 @@ extern "C" {
 // null, A row r is row gather[r] / gdiv of an a_rows-row source (x); else A is [n_rows_max, K].
 // stats (8 int64): violations, accesses, tiles run, tiles missing or run twice, first violation
 // (block, wave, lane, load). Returns the violation count.
+// splits > 1: the split-K down-projection (block b is split b % splits of tile slot b / splits, over K
+// stages [s*nk/S, (s+1)*nk/S)), whose epilogue stores float32 partials to [splits][n_rows_max][nout].
 int64_t moe_check_ffn_loads(const int32_t* off, int E, int n_rows_max, int K, int nout, int dual, int bt,
-                            int ksplit, const int32_t* gather, int gdiv, int64_t a_rows, int64_t* stats) {
+                            int ksplit, const int32_t* gather, int gdiv, int64_t a_rows, int splits, int64_t* stats) {
   Check ck;
   const int bno = dual ? GBR / 2 : GBR;
   const int NT = (nout + bno - 1) / bno;
   const int64_t row_tiles = (n_rows_max + GBM - 1) / GBM + (E < n_rows_max ? E : n_rows_max);
-  const int64_t grid = row_tiles * NT + 8;
-  const int nk = K / GBK;
+  const int64_t grid = (row_tiles * NT + 8) * splits;
+  const int nk_all = K / GBK;
   const int64_t a_extent = (gather ? a_rows : (int64_t)n_rows_max) * K * 2;
   std::vector<int> seen;
   int64_t tiles_expected = 0;
@@ -103,11 +105,16 @@ int64_t moe_check_ffn_loads(const int32_t* off, int E, int n_rows_max, int K, in
   int64_t run = 0;
   for (int64_t b = 0; b < grid; ++b) {
     int e, mt, nt;
-    if (!tile_of(off, E, NT, (int)b, &e, &mt, &nt)) continue;
+    const int s = (int)(b % splits);
+    if (!tile_of(off, E, NT, (int)(b / splits), &e, &mt, &nt)) continue;
     ++run;
     const int cnt = off[e + 1] - off[e];
     const int MT = (cnt + GBM - 1) / GBM;
-    seen[first_tile[e] + (int64_t)mt * NT + nt] += 1;
+    if (s == 0) seen[first_tile[e] + (int64_t)mt * NT + nt] += 1;
+    // the split's stages: its resources start k0 = kt0 * GBK columns in, so stage kt' of the split reads
+    // what stage kt0 + kt' reads unsplit
+    const int kt0 = s * nk_all / splits, kt1 = (s + 1) * nk_all / splits;
+    const int nk = kt1;  // last stage index + 1, in unsplit stage numbers
     const int row0 = off[e] + mt * GBM;
     const int mrows = (GBM < cnt - mt * GBM) ? GBM : cnt - mt * GBM;
     const int n0 = nt * bno;
@@ -131,8 +138,8 @@ int64_t moe_check_ffn_loads(const int32_t* off, int E, int n_rows_max, int K, in
           }
           const uint32_t voff = a_load_off((uint32_t)arow, K, ch);
           ck.wraps(voff, arow * K * 2 + ch * 16, (int)b, w, l, i);
-          for (int kt : {0, nk - 1}) {
-            ck.wraps(voff + stage_soff(kt), (int64_t)voff + (int64_t)kt * GBK * 2, (int)b, w, l, i);
+          for (int kt : {kt0, nk - 1}) {
+            ck.wraps(voff + stage_soff(kt - kt0), (int64_t)voff + (int64_t)(kt - kt0) * GBK * 2, (int)b, w, l, i);
             ck.access(base + voff + stage_soff(kt), 16, a_extent, (int)b, w, l, i);
           }
         }
@@ -144,7 +151,7 @@ int64_t moe_check_ffn_loads(const int32_t* off, int E, int n_rows_max, int K, in
             const uint32_t voff = b_load_off(f, n0, nout, K, ch);
             const int64_t base = ((int64_t)e * nout + n0) * K * 2;
             ck.wraps(voff, (int64_t)(n0 + f < nout ? f : 0) * K * 2 + ch * 16, (int)b, w, l, i);
-            for (int kt : {0, nk - 1})
+            for (int kt : {kt0, nk - 1})
               ck.access(base + voff + stage_soff(kt), 16, (int64_t)E * nout * K * 2, (int)b, w, l, i);
           } else {
             int k, c;
@@ -164,13 +171,22 @@ int64_t moe_check_ffn_loads(const int32_t* off, int E, int n_rows_max, int K, in
           }
         }
       }
-    // epilogue: 16-byte row pieces of rows < mrows, columns n0 + c < nout (c a multiple of 8)
-    for (int c = 0; c < bno; c += 8)
-      if (n0 + c < nout) {
-        ck.access(((int64_t)(row0 + mrows - 1) * nout + n0 + c) * 2, 16, (int64_t)n_rows_max * nout * 2, (int)b,
-                  -1, c, -1);
-        ck.access(((int64_t)row0 * nout + n0 + c) * 2, 16, (int64_t)n_rows_max * nout * 2, (int)b, -1, c, -1);
-      }
+    // epilogue: 16-byte row pieces of rows < mrows, columns n0 + c < nout (c a multiple of 8); split K:
+    // float32 partial pieces of 4 columns into plane s
+    if (splits == 1) {
+      for (int c = 0; c < bno; c += 8)
+        if (n0 + c < nout) {
+          ck.access(((int64_t)(row0 + mrows - 1) * nout + n0 + c) * 2, 16, (int64_t)n_rows_max * nout * 2, (int)b,
+                    -1, c, -1);
+          ck.access(((int64_t)row0 * nout + n0 + c) * 2, 16, (int64_t)n_rows_max * nout * 2, (int)b, -1, c, -1);
+        }
+    } else {
+      const int64_t plane = (int64_t)n_rows_max * nout;
+      for (int c = 0; c < bno; c += 4)
+        if (n0 + c < nout)
+          for (int64_t r : {(int64_t)row0, (int64_t)row0 + mrows - 1})
+            ck.access((s * plane + r * nout + n0 + c) * 4, 16, splits * plane * 4, (int)b, -1, c, -1);
+    }
   }
   int64_t bad_tiles = 0;
   for (int v : seen) bad_tiles += v != 1;

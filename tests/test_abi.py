@@ -54,6 +54,19 @@ def test_capacity_matches_closed_form():
     assert M.moe_capacity(d) == 200
 
 
+def test_split_k_workspace_only_for_tile_starved_down_projections():
+    # the Switch-style layer (C = 320 rows per expert, 16 experts, D = 1024: 64 down-projection tiles,
+    # F = 4096 = 64 stages) splits its reduction 4 ways: 4 planes of T*k x D float32 partials
+    d = M.make_dims(4096, 1024, 16, 1, 4096, capacity_factor=1.25, act=M.MOE_ACT_GELU, dtype=M.MOE_BF16)
+    assert M.moe_workspace_size(d, M.MOE_STAGE_FFN_DOWN) == 4 * 4096 * 1024 * 4
+    assert M.moe_workspace_size(d, M.MOE_STAGE_FFN) == 4096 * 4096 * 2 + 4 * 4096 * 1024 * 4
+    # enough tiles (Mixtral- and DeepSeek-V3-shaped layers), a short F, or float32: no split
+    for dd in (M.make_dims(8192, 4096, 8, 2, 14336, dtype=M.MOE_BF16), M.make_dims(16384, 7168, 256, 8, 2048,
+               dtype=M.MOE_BF16), M.make_dims(4096, 1024, 16, 1, 1024, capacity_factor=1.25, dtype=M.MOE_BF16),
+               M.make_dims(4096, 1024, 16, 1, 4096, capacity_factor=1.25, dtype=M.MOE_F32)):
+        assert M.moe_workspace_size(dd, M.MOE_STAGE_FFN_DOWN) == 0
+
+
 def test_workspace_sizes():
     d = M.make_dims(16384, 7168, 256, 8, 2048)
     assert M.moe_workspace_size(d, M.MOE_STAGE_FFN) >= 16384 * 8 * 2048 * 2

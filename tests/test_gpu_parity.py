@@ -78,9 +78,15 @@ def test_expert_ffn_single_call(name):
     ws = torch.empty(M.moe_workspace_size(d, M.MOE_STAGE_FFN), dtype=torch.uint8, device="cuda")
     y_perm = torch.zeros_like(buf.y_perm)
     M.moe_expert_ffn(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], inp["w2"], y_perm, ws)
+    # the same two halves called one by one (the down-projection split over K where these dims split)
+    h2, y2 = torch.empty_like(buf.h), torch.zeros_like(buf.y_perm)
+    M.moe_expert_ffn_up(d, buf.x_perm, buf.expert_offsets, inp["w1"], inp["w3"], h2)
+    M.moe_expert_ffn_down_splitk(d, h2, buf.expert_offsets, inp["w2"], y2, buf.down_ws)
     torch.cuda.synchronize()
     N = int(buf.expert_offsets[-1])
-    assert torch.equal(y_perm[:N], buf.y_perm[:N]), "moe_expert_ffn differs from up + down"
+    assert torch.equal(y_perm[:N], y2[:N]), "moe_expert_ffn differs from up + down"
+    if buf.down_ws is None:
+        assert torch.equal(y_perm[:N], buf.y_perm[:N]), "moe_expert_ffn differs from the layer's FFN"
     off = P.i64(buf.expert_offsets)
     ref = O.expert_ffn(P.f64(buf.x_perm[:N]), off, host["w1"], host["w3"], host["w2"], cfg.act)
     err = P.rel_err_rows(P.f64(y_perm[:N]), ref[:N])
@@ -95,7 +101,7 @@ def test_deterministic_rerun(name):
     _, b1 = P.run_gpu(cfg, inp)
     _, b2 = P.run_gpu(cfg, inp)
     for key, t in b1.as_dict().items():
-        if t is None or key in ("layout_ws",):
+        if t is None or key in ("layout_ws", "down_ws"):   # scratch
             continue
         t2 = getattr(b2, key)
         if key in ("x_perm", "h", "y_perm"):       # rows past N are unspecified

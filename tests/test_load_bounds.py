@@ -32,7 +32,7 @@ def lib(tmp_path_factory):
     P = ctypes.c_void_p
     L.moe_check_ffn_loads.restype = ctypes.c_int64
     L.moe_check_ffn_loads.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, P]
+                                      ctypes.c_int, ctypes.c_int, P, ctypes.c_int, ctypes.c_int64, ctypes.c_int, P]
     L.moe_check_wgrad_loads.restype = ctypes.c_int64
     L.moe_check_wgrad_loads.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int64, P]
     L.moe_check_route_loads.restype = ctypes.c_int64
@@ -44,12 +44,12 @@ def _ptr(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _ffn(lib, off, n_rows_max, K, nout, dual=False, bt=False, ksplit=0, gather=None, gdiv=1, a_rows=0):
+def _ffn(lib, off, n_rows_max, K, nout, dual=False, bt=False, ksplit=0, gather=None, gdiv=1, a_rows=0, splits=1):
     off = np.ascontiguousarray(off, dtype=np.int32)
     g = None if gather is None else np.ascontiguousarray(gather, dtype=np.int32)
     st = np.zeros(8, dtype=np.int64)
     bad = lib.moe_check_ffn_loads(_ptr(off), len(off) - 1, n_rows_max, K, nout, int(dual), int(bt), ksplit, _ptr(g),
-                                  gdiv, a_rows, _ptr(st))
+                                  gdiv, a_rows, splits, _ptr(st))
     assert st[1] > 0
     assert bad == 0, (f"{st[0]} accesses out of bounds (first: block {st[4]}, wave {st[5]}, lane {st[6]}, "
                       f"load {st[7]}), {st[3]} tiles not run exactly once")
@@ -75,6 +75,9 @@ def _check_layer(lib, cfg, counts, rng):
     _ffn(lib, off, P_, D, F, dual=dual)
     _ffn(lib, off, P_, D, F, dual=dual, gather=r2p, gdiv=k, a_rows=T)
     _ffn(lib, off, P_, F, D)
+    if F % 64 == 0 and F // 64 >= 32:
+        for S in (2, 4, 8):   # the split-K down-projection
+            _ffn(lib, off, P_, F, D, splits=S)
     # training forward (pre-activations stored: same loads) and the data-gradient GEMMs on the weights
     # as stored: dh = dy_perm W2 (W2[e] read K-major as [D][F]); dx_perm = [da1 da3] [W1; W3] (K-major,
     # the reduction split between W1 and W3 at F)
@@ -153,10 +156,10 @@ def test_checker_catches_a_bad_offset(lib):
     # the check itself: one more expert's worth of rows than the operand holds must be reported
     off = np.array([0, 320, 700], dtype=np.int32)
     st = np.zeros(8, dtype=np.int64)
-    bad = lib.moe_check_ffn_loads(_ptr(off), 2, 600, 128, 256, 0, 0, 0, None, 1, 0, _ptr(st))
+    bad = lib.moe_check_ffn_loads(_ptr(off), 2, 600, 128, 256, 0, 0, 0, None, 1, 0, 1, _ptr(st))
     assert bad > 0 and st[0] > 0
     # and a gather index past the source rows
     off = np.array([0, 4], dtype=np.int32)
     g = np.array([0, 1, 2, 1000], dtype=np.int32)
-    bad = lib.moe_check_ffn_loads(_ptr(off), 1, 4, 128, 256, 0, 0, 0, _ptr(g), 1, 8, _ptr(st))
+    bad = lib.moe_check_ffn_loads(_ptr(off), 1, 4, 128, 256, 0, 0, 0, _ptr(g), 1, 8, 1, _ptr(st))
     assert bad > 0
