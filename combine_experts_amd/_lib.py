@@ -45,7 +45,8 @@ class moe_layer_args(ctypes.Structure):
                                   "expert_offsets", "rank_counts", "rank_offsets", "layout_ws")] + \
         [("layout_ws_bytes", ctypes.c_size_t)] + \
         [(n, _P) for n in ("shared_w1", "shared_w3", "shared_w2")] + [("shared_F", ctypes.c_int32)] + \
-        [(n, _P) for n in ("shared_h", "shared_y", "shared_offsets", "logits", "pre")]
+        [(n, _P) for n in ("shared_h", "shared_y", "shared_offsets", "logits", "pre", "down_ws")] + \
+        [("down_ws_bytes", ctypes.c_size_t)]
 
 
 class moe_backward_args(ctypes.Structure):

@@ -95,7 +95,9 @@ int moe_layer_forward(const moe_dims* d, const moe_layer_args* a, int32_t n_chun
     } else if ((st = moe_expert_ffn_up_gather(&c, xc, a->row_to_pair + p0, eoff, a->w1, a->w3, hc, fs)) != MOE_OK) {
       return st;
     }
-    if ((st = moe_expert_ffn_down(&c, hc, eoff, a->w2, yp, fs)) != MOE_OK) return st;
+    st = a->down_ws ? moe_expert_ffn_down_splitk(&c, hc, eoff, a->w2, yp, a->down_ws, a->down_ws_bytes, fs)
+                    : moe_expert_ffn_down(&c, hc, eoff, a->w2, yp, fs);
+    if (st != MOE_OK) return st;
     if (two && hipEventRecord(events[2 * ci + 1], side_stream) != hipSuccess) return MOE_ERR_HIP;
     if (a->shared_w1 != nullptr) {
       void* sh = static_cast<char*>(a->shared_h) + ci * tc * (int64_t)a->shared_F * eb;

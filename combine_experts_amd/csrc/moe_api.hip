@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 107;
+constexpr int kAbiVersion = 108;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }

@@ -58,6 +58,8 @@ def _layer_args(buf: MoELayerBuffers, x, w_gate, bias, w1, w3, w2, pre=None) -> 
         setattr(a, n, _ptr(getattr(buf, n)))
     a.layout_ws_bytes = buf.layout_ws.numel()
     a.pre = _ptr(pre)
+    if buf.down_ws is not None:
+        a.down_ws, a.down_ws_bytes = buf.down_ws.data_ptr(), buf.down_ws.numel()
     return a
 
 
@@ -74,8 +76,10 @@ class LayerExecutor:
     shared expert). Allocates once with torch; every call only enqueues the library's kernels."""
 
     def __init__(self, d: L.moe_dims, n_chunks: int = 1, two_streams: bool = False, shared_F: int = 0,
-                 device="cuda", gather: bool = False):
-        """gather=True: no x_perm buffer; each micro-batch's up-projection reads its rows from x."""
+                 device="cuda", gather: bool = False, split_k: bool = True):
+        """gather=True: no x_perm buffer; each micro-batch's up-projection reads its rows from x.
+        split_k=False: no split-K workspace, so the down-projection never splits and any number of
+        micro-batches gives the whole batch's bits."""
         if d.T % n_chunks != 0:
             raise ValueError("T must split evenly into the micro-batches")
         self.d, self.n_chunks = d, n_chunks
@@ -98,6 +102,9 @@ class LayerExecutor:
         dc.T = d.T // n_chunks
         ws = (L.moe_workspace_size(dc, L.MOE_STAGE_LAYOUT) + 255) // 256 * 256
         self.layout_ws = torch.empty(max(1, ws * n_chunks), dtype=torch.uint8, device=device)
+        # split-K scratch of the micro-batches' down-projections (they run one after another on one stream)
+        n = L.moe_workspace_size(dc, L.MOE_STAGE_FFN_DOWN) if split_k else 0
+        self.down_ws = torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
         self.shared_F = shared_F
         if shared_F > 0:
             self.shared_h = torch.empty((d.T, shared_F), dtype=dt, device=device)
@@ -123,6 +130,8 @@ class LayerExecutor:
                   "expert_offsets", "rank_counts", "rank_offsets", "layout_ws"):
             setattr(a, n, p(getattr(self, n)))
         a.layout_ws_bytes = self.layout_ws.numel()
+        if self.down_ws is not None:
+            a.down_ws, a.down_ws_bytes = self.down_ws.data_ptr(), self.down_ws.numel()
         if shared is not None:
             if self.shared_F <= 0:
                 raise ValueError("executor built without a shared expert")

@@ -228,8 +228,8 @@ int moe_expert_ffn_down(const moe_dims* d, const void* h, const int32_t* expert_
  * rounding only). bf16 only; S > 1 when F >= 2048 and the layer has at most 64 such tiles.
  *   ws, ws_bytes  moe_workspace_size(MOE_STAGE_FFN_DOWN) bytes: S x T*top_k x D float32 partials. When
  *                 that size is 0, or ws is NULL, this is moe_expert_ffn_down.
- * Other arguments as moe_expert_ffn_down. The layer executor does not split (its micro-batches then give
- * the same bits as the whole batch). */
+ * Other arguments as moe_expert_ffn_down. The layer executor splits only when its caller hands it such a
+ * workspace (moe_layer_args.down_ws); without one its micro-batches give the same bits as the whole batch. */
 int moe_expert_ffn_down_splitk(const moe_dims* d, const void* h, const int32_t* expert_offsets, const void* w2,
                                void* y_perm, void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -357,6 +357,13 @@ typedef struct moe_layer_args {
    * (pre: bf16 only) */
   float* logits;
   void* pre;
+  /* optional split-K scratch of the down-projection, or NULL (no split): each micro-batch's
+   * down-projection runs as moe_expert_ffn_down_splitk at T = T/n_chunks with this workspace, which
+   * must hold moe_workspace_size(MOE_STAGE_FFN_DOWN) at that T (else MOE_ERR_WORKSPACE) and be 16-byte
+   * aligned. The micro-batches' FFNs run one after another on one stream, so one region serves them
+   * all. With it, micro-batches give the whole batch's bits only where both split the same way. */
+  void* down_ws;
+  size_t down_ws_bytes;
 } moe_layer_args;
 
 /* Runs the layer as above. side_stream NULL: everything on `stream`, micro-batch after micro-batch.

@@ -28,9 +28,13 @@ def to_host(inp):
     return {k: (None if v is None else v.detach().cpu()) for k, v in inp.items()}
 
 
-def run_gpu(cfg, inp, logits=True):
+def run_gpu(cfg, inp, logits=True, split_k=True):
+    """The layer forward; split_k=False drops the split-K workspace, so the down-projection runs
+    unsplit wherever it would split."""
     d = M.dims_from_config(cfg)
     buf = M.MoELayerBuffers(d, device="cuda", logits=logits)
+    if not split_k:
+        buf.down_ws = None
     M.forward(buf, inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
     torch.cuda.synchronize()
     return d, buf

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert M.moe_abi_version() == 107
+    assert M.moe_abi_version() == 108
     for s in range(5):
         assert M.moe_status_str(s).startswith("MOE_")
     assert "unknown" in M.moe_status_str(99)
@@ -227,10 +227,11 @@ def test_cluster_and_padded_host_checks():
 
 
 def test_layer_args_struct_layout():
-    # 19 pointers, a size_t, 3 pointers, an int32 (padded to 8), 5 pointers
-    assert ctypes.sizeof(M.moe_layer_args) == 19 * 8 + 8 + 3 * 8 + 8 + 5 * 8
+    # 19 pointers, a size_t, 3 pointers, an int32 (padded to 8), 6 pointers, a size_t
+    assert ctypes.sizeof(M.moe_layer_args) == 19 * 8 + 8 + 3 * 8 + 8 + 6 * 8 + 8
     assert M.moe_layer_args.layout_ws_bytes.offset == 19 * 8
     assert M.moe_layer_args.shared_F.offset == 19 * 8 + 8 + 3 * 8
+    assert M.moe_layer_args.down_ws.offset == 19 * 8 + 8 + 3 * 8 + 8 + 5 * 8
 
 
 def test_layer_forward_host_checks():

@@ -2,7 +2,9 @@
 
 Micro-batching changes only which rows share an expert group and when each step runs; every
 token's route, every row's FFN and every token's combine meet the same kernels with the same
-operands, so the overlapped executor must equal the plain layer bit for bit. The shared expert is
+operands, so the overlapped executor must equal the plain layer bit for bit. (A split-K
+down-projection splits by the micro-batch's own tile count, so these comparisons run without the
+split-K workspace; its own tests cover it.) The shared expert is
 checked against the oracle's float64 layer (routed sum + shared expert) on decisive tokens.
 """
 import numpy as np
@@ -37,10 +39,10 @@ def test_micro_batches_on_two_streams_equal_the_plain_layer(name):
     cfg = CASES[name]
     print(f"[overlap] {name}: {cfg}", flush=True)
     inp = W.make_inputs(cfg, "cuda")
-    _, buf = P.run_gpu(cfg, inp, logits=False)
+    _, buf = P.run_gpu(cfg, inp, logits=False, split_k=False)
     d = M.dims_from_config(cfg)
     for n_chunks, two in ((1, False), (2, False), (2, True), (4, True)):
-        ex = M.LayerExecutor(d, n_chunks=n_chunks, two_streams=two)
+        ex = M.LayerExecutor(d, n_chunks=n_chunks, two_streams=two, split_k=False)
         y = ex.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
         torch.cuda.synchronize()
         assert torch.equal(y, buf.y), f"{n_chunks} micro-batches, two streams={two}"
@@ -68,7 +70,7 @@ def test_shared_expert_layer(name):
     inp = W.make_inputs(cfg, "cuda")
     host = P.to_host(inp)
     d = M.dims_from_config(cfg)
-    ex1 = M.LayerExecutor(d, n_chunks=1, shared_F=cfg.shared_F)
+    ex1 = M.LayerExecutor(d, n_chunks=1, shared_F=cfg.shared_F, split_k=False)
     y1 = ex1.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], shared=_shared(inp)).clone()
     torch.cuda.synchronize()
     # against the oracle's float64 layer (routed + shared) on decisive tokens
@@ -83,7 +85,7 @@ def test_shared_expert_layer(name):
     assert err_s.max() <= P.TOL_Y[cfg.dtype], f"shared expert: max rel err {err_s.max():.3e}"
     # micro-batches on two streams: bit for bit the same
     for n_chunks in (2, 4):
-        ex = M.LayerExecutor(d, n_chunks=n_chunks, two_streams=True, shared_F=cfg.shared_F)
+        ex = M.LayerExecutor(d, n_chunks=n_chunks, two_streams=True, shared_F=cfg.shared_F, split_k=False)
         y = ex.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], shared=_shared(inp))
         torch.cuda.synchronize()
         assert torch.equal(y, y1), f"{n_chunks} micro-batches with the shared expert"
@@ -115,10 +117,10 @@ def test_overlapped_full_dsv3_with_shared_expert():
     print(f"[overlap] full dsv3 + shared expert", flush=True)
     inp = W.make_inputs(cfg, "cuda")
     d = M.dims_from_config(cfg)
-    ex1 = M.LayerExecutor(d, n_chunks=1, shared_F=cfg.shared_F)
+    ex1 = M.LayerExecutor(d, n_chunks=1, shared_F=cfg.shared_F, split_k=False)
     y1 = ex1.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], shared=_shared(inp)).clone()
     del ex1
-    ex2 = M.LayerExecutor(d, n_chunks=2, two_streams=True, shared_F=cfg.shared_F)
+    ex2 = M.LayerExecutor(d, n_chunks=2, two_streams=True, shared_F=cfg.shared_F, split_k=False)
     y2 = ex2.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"], shared=_shared(inp))
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)

@@ -85,8 +85,7 @@ def test_expert_ffn_single_call(name):
     torch.cuda.synchronize()
     N = int(buf.expert_offsets[-1])
     assert torch.equal(y_perm[:N], y2[:N]), "moe_expert_ffn differs from up + down"
-    if buf.down_ws is None:
-        assert torch.equal(y_perm[:N], buf.y_perm[:N]), "moe_expert_ffn differs from the layer's FFN"
+    assert torch.equal(y_perm[:N], buf.y_perm[:N]), "moe_expert_ffn differs from the layer's FFN"
     off = P.i64(buf.expert_offsets)
     ref = O.expert_ffn(P.f64(buf.x_perm[:N]), off, host["w1"], host["w3"], host["w2"], cfg.act)
     err = P.rel_err_rows(P.f64(y_perm[:N]), ref[:N])

@@ -36,7 +36,7 @@ def test_split_k_down_projection(name):
     assert n_ws > 0, "these dims are expected to take the split-K path"
     print(f"[splitk] {name}: {cfg} workspace {n_ws / 2**20:.1f} MiB", flush=True)
     inp = W.make_inputs(cfg, "cuda")
-    d, buf = P.run_gpu(cfg, inp)          # the layer (unsplit down-projection) fills h, y_perm
+    d, buf = P.run_gpu(cfg, inp, split_k=False)   # the layer with the unsplit down-projection fills h, y_perm
     ws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
     y1 = torch.zeros_like(buf.y_perm)
     y2 = torch.zeros_like(buf.y_perm)
@@ -88,3 +88,59 @@ def test_split_k_layer_end_to_end():
     s = dec["set"]
     err = P.rel_err_rows(P.f64(buf.y)[s], ref["y"][s])
     assert err.max() <= P.TOL_Y[cfg.dtype], f"end to end: {err.max():.3e}"
+
+
+@needs_gpu
+def test_layer_forward_splits_with_a_workspace():
+    """moe_layer_forward handed the split-K workspace: the staged entry points' bits with
+    moe_expert_ffn_down_splitk, through forward() and a one-micro-batch executor on two streams; without
+    the workspace, the unsplit down-projection's bits."""
+    cfg = CASES["switch_cap"]
+    inp = W.make_inputs(cfg, "cuda")
+    args = (inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    d = M.dims_from_config(cfg)
+    buf = M.MoELayerBuffers(d, device="cuda")
+    assert buf.down_ws is not None
+    M.forward(buf, *args)
+    st = M.MoELayerBuffers(d, device="cuda")
+    M.moe_route(d, inp["x"], inp["w_gate"], inp["bias"], st.topk_idx, st.topk_gate, None)
+    M.moe_dispatch_layout(d, st.topk_idx, st.expert_counts, st.expert_offsets, st.rank_counts, st.rank_offsets,
+                          st.pair_to_row, st.row_to_pair, st.layout_ws)
+    M.moe_permute(d, inp["x"], st.pair_to_row, st.x_perm)
+    M.moe_expert_ffn_up(d, st.x_perm, st.expert_offsets, inp["w1"], inp["w3"], st.h)
+    M.moe_expert_ffn_down_splitk(d, st.h, st.expert_offsets, inp["w2"], st.y_perm, st.down_ws)
+    M.moe_unpermute_combine(d, st.y_perm, st.pair_to_row, st.topk_gate, st.y)
+    ex = M.LayerExecutor(d, n_chunks=1, two_streams=True)
+    assert ex.down_ws is not None
+    y_ex = ex.forward(*args).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(buf.y, st.y), "forward() differs from the staged split-K path"
+    assert torch.equal(y_ex, st.y), "executor differs from the staged split-K path"
+    # without the workspace the executor runs the unsplit down-projection
+    ex.down_ws = None
+    y0 = ex.forward(*args).clone()
+    M.moe_expert_ffn_down(d, st.h, st.expert_offsets, inp["w2"], st.y_perm)
+    M.moe_unpermute_combine(d, st.y_perm, st.pair_to_row, st.topk_gate, st.y)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, st.y), "executor without the workspace differs from the unsplit path"
+    assert not torch.equal(y0, y_ex), "the split and unsplit sums are expected to round differently somewhere"
+
+
+@needs_gpu
+def test_micro_batches_share_one_split_k_workspace():
+    """Four micro-batches on two streams whose down-projections split (each at its own T) and reuse
+    one workspace in turn: each micro-batch's rows are the bits of the layer run on that micro-batch
+    alone."""
+    cfg = W.get_config("switch_cap", T=1024, capacity_factor=0.0)
+    n_chunks, tc = 4, 256
+    inp = W.make_inputs(cfg, "cuda")
+    args = (inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
+    ex = M.LayerExecutor(M.dims_from_config(cfg), n_chunks=n_chunks, two_streams=True)
+    assert ex.down_ws is not None, "a 256-token micro-batch of these dims is expected to split"
+    y = ex.forward(inp["x"], *args).clone()
+    dc = M.dims_from_config(cfg.replace(T=tc))
+    for ci in range(n_chunks):
+        one = M.MoELayerBuffers(dc, device="cuda")
+        M.forward(one, inp["x"][ci * tc:(ci + 1) * tc].contiguous(), *args)
+        torch.cuda.synchronize()
+        assert torch.equal(y[ci * tc:(ci + 1) * tc], one.y), f"micro-batch {ci}"
