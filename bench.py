@@ -32,21 +32,29 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 STAGES = ["route", "layout", "ffn_up", "ffn_down", "combine"]   # ffn_up includes the permute
 DOMINANT = "ffn_up"
-DOMINANT_SRC = os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip")
+# what the dominant kernel's machine code is built from: its source, its geometry header and the build
+# flags; the committed PMC traffic summary is used only while these are unchanged
+DOMINANT_SRC = (os.path.join(ROOT, "combine_experts_amd", "csrc", "ffn.hip"),
+                os.path.join(ROOT, "combine_experts_amd", "csrc", "gemm_geometry.h"),
+                os.path.join(ROOT, "combine_experts_amd", "build.py"))
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3 PMC summary, or None
-    if there is none or the kernel source changed since the counters were taken."""
+    if there is none or the kernel's source, geometry header or build flags changed since the counters
+    were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_ffn_up_{workload}.txt")
     if not os.path.exists(path):
         return None

@@ -22,6 +22,9 @@ FLAGS = [
     # packed fp32 instructions stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    # device code only: the machine scheduler's iterative ILP strategy (measured against the default:
+    # grouped GEMMs 0.6-2.6 % faster, the router 7 % at the Mixtral shape, same bits)
+    "-Xarch_device", "-mllvm=--amdgpu-sched-strategy=iterative-ilp",
 ]
 
 
