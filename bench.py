@@ -359,7 +359,7 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures the one-GPU share of the MoE layer only: run it with --gpus 1 "
-              "(multi-GPU expert parallelism is not part of this build).", file=sys.stderr)
+              "(the library runs one GPU's share; multi-GPU expert parallelism is not implemented).", file=sys.stderr)
         return 2
 
     import torch

@@ -101,7 +101,7 @@ const char* moe_status_str(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK";
     case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer, inconsistent dims or misaligned pointer";
-    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid dims with no kernel in this build";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: valid dims that no kernel of this library handles";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: kernel launch failed";
     default: return "unknown moe status";

@@ -52,7 +52,7 @@ extern "C" {
 enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = 1, /* null required pointer, inconsistent dims, misaligned pointer */
-  MOE_ERR_UNSUPPORTED = 2, /* valid dims this build has no kernel for (see each entry point) */
+  MOE_ERR_UNSUPPORTED = 2, /* valid dims no kernel of this library handles (see each entry point) */
   MOE_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than moe_workspace_size() */
   MOE_ERR_HIP = 4          /* a kernel launch failed */
 };
