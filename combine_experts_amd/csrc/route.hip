@@ -208,8 +208,11 @@ __device__ __forceinline__ void logits_f32(const float* __restrict__ x, const fl
   }
 }
 
+// (ov, oe) ranks above (v, e): larger value, or the same value and a lower index. Bitwise operators,
+// not short-circuit ones, so that the comparison and the selects that use it compile to straight-line
+// vector code rather than a branch per element.
 __device__ __forceinline__ bool better(float v, int e, float ov, int oe) {
-  return ov > v || (ov == v && oe < e);
+  return (ov > v) | ((ov == v) & (oe < e));
 }
 
 // The same register of another lane of this lane's 16-lane row, through DPP (a modifier of a VALU
@@ -230,10 +233,9 @@ template <int CTRL>
 __device__ __forceinline__ void argmax_step(float& bv, int& be) {
   const float ov = dpp_f<CTRL>(bv);
   const int oe = dpp_i<CTRL>(be);
-  if (better(bv, be, ov, oe)) {
-    bv = ov;
-    be = oe;
-  }
+  const bool t = better(bv, be, ov, oe);
+  bv = t ? ov : bv;
+  be = t ? oe : be;
 }
 // (value, -index) maximum over the 16-lane row, in every lane of the row
 __device__ __forceinline__ void argmax16(float& bv, int& be) {
@@ -343,11 +345,10 @@ __device__ __forceinline__ void select_token(const float* lrow, int E, int k, in
                                       : ((gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(lv) : lv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          if (j < per && sv > best[j]) {
-            const float tmp = best[j];
-            best[j] = sv;
-            sv = tmp;
-          }
+          const bool t = (j < per) & (sv > best[j]);
+          const float bj = best[j];
+          best[j] = t ? sv : bj;
+          sv = t ? bj : sv;
         }
       }
       gs = 0.f;
@@ -359,15 +360,14 @@ __device__ __forceinline__ void select_token(const float* lrow, int E, int k, in
     int rank = 0;
     for (int g = 0; g < n_groups; ++g) {
       const float og = __shfl(gs, g, MOE_WAVE);
-      if (og > gs || (og == gs && g < lane)) ++rank;
+      rank += ((og > gs) | ((og == gs) & (g < lane))) ? 1 : 0;
     }
-    const bool gkeep = (lane < n_groups) && (rank < topk_groups);
+    const bool gkeep = (lane < n_groups) & (rank < topk_groups);
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
       const int e = lane + i * MOE_WAVE;
       const int g = (e < E) ? e / gsize : 0;
-      const bool keep = __shfl((int)gkeep, g, MOE_WAVE) != 0;
-      if (!keep) ok[i] = false;
+      ok[i] = ok[i] & (__shfl((int)gkeep, g, MOE_WAVE) != 0);
     }
   }
   // k rounds of wave-wide argmax; lane j keeps slot j
@@ -378,24 +378,20 @@ __device__ __forceinline__ void select_token(const float* lrow, int E, int k, in
     int be = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + i * MOE_WAVE;
-      if (ok[i] && better(bv, be, key[i], e)) {
-        bv = key[i];
-        be = e;
-      }
+      const bool t = ok[i] & better(bv, be, key[i], lane + i * MOE_WAVE);
+      bv = t ? key[i] : bv;
+      be = t ? lane + i * MOE_WAVE : be;
     }
 #pragma unroll
     for (int off = MOE_WAVE / 2; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off, MOE_WAVE);
       const int oe = __shfl_xor(be, off, MOE_WAVE);
-      if (better(bv, be, ov, oe)) {
-        bv = ov;
-        be = oe;
-      }
+      const bool t = better(bv, be, ov, oe);
+      bv = t ? ov : bv;
+      be = t ? oe : be;
     }
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (lane + i * MOE_WAVE == be) ok[i] = false;
+    for (int i = 0; i < kMaxPerLane; ++i) ok[i] = ok[i] & (lane + i * MOE_WAVE != be);
     if (lane == j) {
       my_v = bv;
       my_e = be;
@@ -504,11 +500,10 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
         float sv = has_sb ? key[i] : v[i];
 #pragma unroll
         for (int j = 0; j < P; ++j) {
-          if ((P <= 2 || j < per) && sv > best[j]) {
-            const float t = best[j];
-            best[j] = sv;
-            sv = t;
-          }
+          const bool t = (P <= 2 || j < per) & (sv > best[j]);
+          const float bj = best[j];
+          best[j] = t ? sv : bj;
+          sv = t ? bj : sv;
         }
       }
       // merge sorted lists across the lanes of the group (lpg lanes: 1, 2, 4, 8 or 16)
@@ -551,14 +546,14 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
                                 : group_score(std::integral_constant<int, 8>{});
     const int my_g = L / lpg;
     int rank = 0;
-    for (int g = 0; g < n_groups; ++g) {
-      const float og = __shfl(gs, seg * 16 + g * lpg, MOE_WAVE);
-      if (og > gs || (og == gs && g < my_g)) ++rank;
-    }
-    if (rank >= topk_groups) {
 #pragma unroll
-      for (int i = 0; i < NT; ++i) ok[i] = false;
+    for (int g = 0; g < 16; ++g) {  // n_groups <= 16 here; the reads are issued together
+      const float og = __shfl(gs, seg * 16 + g * lpg, MOE_WAVE);
+      rank += ((g < n_groups) & ((og > gs) | ((og == gs) & (g < my_g)))) ? 1 : 0;
     }
+    const bool gkeep = rank < topk_groups;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) ok[i] = ok[i] & gkeep;
   }
   // k rounds of a segment-wide argmax on (value, -expert); lane j of the segment keeps slot j
   float my_v = 0.f;
@@ -568,16 +563,13 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
     int be = 0x7fffffff;
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-      const int e = L * NT + i;
-      if (ok[i] && better(bv, be, key[i], e)) {
-        bv = key[i];
-        be = e;
-      }
+      const bool t = ok[i] & better(bv, be, key[i], L * NT + i);
+      bv = t ? key[i] : bv;
+      be = t ? L * NT + i : be;
     }
     argmax16(bv, be);
 #pragma unroll
-    for (int i = 0; i < NT; ++i)
-      if (L * NT + i == be) ok[i] = false;
+    for (int i = 0; i < NT; ++i) ok[i] = ok[i] & (L * NT + i != be);
     if (L == j) {
       my_v = bv;
       my_e = be;
@@ -602,7 +594,12 @@ __device__ __forceinline__ void select4(const float* lds_logits, int trow0, int 
     denom = z;
   } else {
     if (L < k) w = (gate == MOE_GATE_SIGMOID_TOPK) ? sigmoidf_(my_v) : expf(my_v - v0);
-    for (int j = 0; j < k; ++j) denom += __shfl(w, seg * 16 + j, MOE_WAVE);  // slot order
+    // slot order 0 .. k-1 (k <= 16 here); the slots past k add exact zeros
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float wj = __shfl(w, seg * 16 + j, MOE_WAVE);
+      denom += (j < k) ? wj : 0.f;
+    }
   }
   if (tok_ok && L < k) {
     out_idx[seg * k + L] = my_e;
