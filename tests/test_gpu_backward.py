@@ -74,6 +74,44 @@ CASES = {
 }
 
 
+def _random_config(i):
+    """bf16 layer dims number i for the backward: a seeded draw over expert counts, top-k, the three
+    gate forms, group limits, capacity cuts, selection-free biases and both activations."""
+    rng = np.random.default_rng(3000 + i)
+    E = int(rng.choice([2, 3, 5, 8, 12, 16, 24, 32, 64, 96, 128, 256]))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    n_groups = topk_groups = 0
+    if E >= 4 and rng.random() < 0.4:
+        opts = [g for g in range(2, min(E, 64) + 1) if E % g == 0 and g < E]
+        if opts:
+            n_groups = int(rng.choice(opts))
+            topk_groups = int(rng.integers(max(1, -(-k // (E // n_groups))), n_groups + 1))
+    return W.MoEConfig(
+        name=f"random{i}", T=int(rng.choice([33, 64, 65, 127, 200, 333])), D=64 * int(rng.integers(1, 5)), E=E,
+        top_k=k, F=64 * int(rng.integers(1, 6)), act=int(rng.choice([W.ACT_SWIGLU, W.ACT_GELU])),
+        gate=int(rng.choice([W.GATE_SOFTMAX_TOPK, W.GATE_SIGMOID_TOPK, W.GATE_SOFTMAX_FULL])),
+        capacity_factor=float(rng.choice([0.0, 0.0, 0.5, 1.25])), n_groups=n_groups, topk_groups=topk_groups,
+        bias=str(rng.choice(["none", "normal0.5"])), seed=4000 + i)
+
+
+N_RANDOM = 8
+for _i in range(N_RANDOM):
+    CASES[f"random{_i}"] = _random_config(_i)
+
+
+def test_random_backward_configs_are_valid():
+    # (host only) the draws are valid layer dims and cover every gate form, both activations, group
+    # limits and capacity cuts
+    cfgs = [_random_config(i) for i in range(N_RANDOM)]
+    for c in cfgs:
+        assert 1 <= c.top_k <= min(c.E, 8) and c.D % 64 == 0 and c.F % 64 == 0
+        if c.n_groups:
+            assert c.E % c.n_groups == 0 and c.topk_groups * (c.E // c.n_groups) >= c.top_k
+    assert {c.gate for c in cfgs} == {W.GATE_SOFTMAX_TOPK, W.GATE_SIGMOID_TOPK, W.GATE_SOFTMAX_FULL}
+    assert {c.act for c in cfgs} == {W.ACT_SWIGLU, W.ACT_GELU}
+    assert any(c.n_groups for c in cfgs) and any(c.capacity_factor > 0 for c in cfgs)
+
+
 def _nm(cfg):
     return 2 if cfg.act == W.ACT_SWIGLU else 1
 
