@@ -20,10 +20,20 @@ Pages cited (titles as they appear on the pages):
             Dispatch, Capacity Factors, and Parallel Folding Scale MoE
             Architectures" (llms.blog)
 
-Parity status per function (what pins each one is in ``tests/test_oracle_pins.py``):
-  route_logits, select_topk, select_group_limited, gate_weights,
-  capacity, dispatch_layout, send_counts, dispatch_matrix, permute,
-  expert_ffn, expert_ffn_rows, combine, comm_volume: pinned.
+Parity status per function (the tests that pin each one):
+  tests/test_oracle_pins.py: route_logits, route, select_topk, group_scores,
+    select_group_limited, gate_weights, decisive_tokens, selection_key,
+    round_to_f32, capacity, dispatch_layout, send_counts, dispatch_matrix,
+    dispatch_volume_bytes, comm_volume_elements, permute, expert_ffn,
+    expert_ffn_rows, silu, gelu, combine, layer_forward: pinned.
+  tests/test_oracle_backward.py: layer_backward, gate_weights_backward,
+    silu_grad, gelu_grad (central differences): pinned.
+  tests/test_oracle_balance.py: router_probabilities, load_balance_stats,
+    update_select_bias: pinned.
+  tests/test_oracle_cluster.py: source_shards, recv_layout, cluster_forward,
+    padded_layout, permute_padded, shared_expert_ffn, layer_forward_chunked:
+    pinned.
+  as_f64 is an exact upcast (no arithmetic).
   The absolute float values of y at the five workload shapes: parity unpinned
   (no page prints a numeric worked example of y; they are pinned only through
   the special cases and invariants in the tests).

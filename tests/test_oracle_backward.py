@@ -103,3 +103,28 @@ def test_activation_derivatives_against_differences():
     for f, df in ((O.silu, O.silu_grad), (O.gelu, O.gelu_grad)):
         num = (f(a + 1e-6) - f(a - 1e-6)) / 2e-6
         np.testing.assert_allclose(df(a), num, rtol=1e-7, atol=1e-9)
+
+
+@pytest.mark.parametrize("mode", [W.GATE_SOFTMAX_TOPK, W.GATE_SIGMOID_TOPK, W.GATE_SOFTMAX_FULL])
+def test_gate_weights_backward_against_differences(mode):
+    # dl[t, e] = sum_j dgate[t, j] * d g[t, j] / d l[t, e] with the selection held fixed, each
+    # derivative by a central difference of gate_weights itself (no layer around it)
+    rng = np.random.default_rng(11 + mode)
+    T, E, k = 5, 7, 3
+    l = rng.normal(0.0, 1.5, (T, E))
+    idx = np.argsort(-l, axis=1)[:, :k]
+    dg = rng.normal(0.0, 1.0, (T, k))
+    got = O.gate_weights_backward(l, idx, mode, dg)
+    eps = 1e-6
+    want = np.zeros((T, E))
+    for e in range(E):
+        lp, lm = l.copy(), l.copy()
+        lp[:, e] += eps
+        lm[:, e] -= eps
+        want[:, e] = ((O.gate_weights(lp, idx, mode) - O.gate_weights(lm, idx, mode)) * dg).sum(axis=1) / (2 * eps)
+    np.testing.assert_allclose(got, want, rtol=1e-7, atol=1e-9)
+    if mode != W.GATE_SOFTMAX_FULL:
+        # only the selected logits move renormalised top-k gates
+        unsel = np.ones((T, E), dtype=bool)
+        np.put_along_axis(unsel, idx, False, axis=1)
+        assert np.all(got[unsel] == 0)

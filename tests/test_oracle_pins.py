@@ -632,3 +632,26 @@ def test_identical_experts_make_a_dense_ffn(act):
             h = [0.5 * a[f] * (1.0 + math.erf(a[f] / math.sqrt(2.0))) for f in range(cfg.F)]
         want = [sum(w2[d][f] * h[f] for f in range(cfg.F)) for d in range(cfg.D)]
         np.testing.assert_allclose(out["y"][t], want, rtol=1e-11, atol=1e-12)
+
+
+def test_round_to_f32_ties_to_even():
+    # 1 + 2^-24 lies halfway between 1 and the next float32 (1 + 2^-23): the even one, 1, wins;
+    # 1 + 3*2^-24 lies halfway between 1 + 2^-23 and 1 + 2^-22: again the even mantissa, 1 + 2^-22
+    got = O.round_to_f32(np.array([1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, -(1 + 2.0 ** -24), 0.1]))
+    assert got[0] == 1.0 and got[1] == 1 + 2.0 ** -22 and got[2] == -1.0
+    assert got[3] == float(np.float32(0.1)) and got[3] != 0.1
+
+
+def test_selection_key_hand_values():
+    # sigmoid gating ranks sigmoid(l) + b, the other gates l + b; each term held in float32
+    l = np.array([[0.0, 2.0, -1.0]])
+    b = np.array([0.25, -0.5, 1e-9], dtype=np.float32)
+    sig = O.selection_key(l, O.GATE_SIGMOID_TOPK, b)
+    s2 = float(np.float32(1.0 / (1.0 + np.exp(-2.0))))
+    s_1 = float(np.float32(1.0 / (1.0 + np.exp(1.0))))
+    assert sig[0, 0] == 0.75
+    assert sig[0, 1] == float(np.float32(s2 - 0.5))
+    assert sig[0, 2] == float(np.float32(s_1 + float(np.float32(1e-9))))
+    soft = O.selection_key(l, O.GATE_SOFTMAX_TOPK, b)
+    assert soft[0, 0] == 0.25 and soft[0, 1] == 1.5
+    assert soft[0, 2] == -1.0  # 1e-9 is below half an ulp of 1 in float32: the sum rounds back to -1
