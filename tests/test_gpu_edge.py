@@ -1,6 +1,6 @@
 """Edge cases of the newer paths on the GPU: an empty batch through the executor, the cluster view,
 the padded layout and the backward (every gradient exactly zero); experts that receive no rows in
-the backward; a micro-batch count equal to the token count."""
+the backward; a micro-batch count equal to the token count; a layer at the largest top-k (32)."""
 import numpy as np
 import pytest
 import torch
@@ -95,3 +95,23 @@ def test_one_token_per_micro_batch():
     y = ex.forward(inp["x"], inp["w_gate"], inp["bias"], inp["w1"], inp["w3"], inp["w2"])
     torch.cuda.synchronize()
     assert torch.equal(y, buf.y)
+
+
+@needs_gpu
+@pytest.mark.parametrize("cf", [0.0, 0.75])
+def test_layer_with_the_largest_top_k(cf):
+    # k = 32, the router's largest: the general selection, combine and layout paths, every stage
+    # against the oracle (with a capacity cut too)
+    cfg = W.MoEConfig(name=f"k32_cf{cf}", T=100, D=64, E=48, top_k=32, F=64, ep_size=4, capacity_factor=cf,
+                      seed=72)
+    print(f"[edge] {cfg.name}", flush=True)
+    inp = W.make_inputs(cfg, "cuda")
+    host = P.to_host(inp)
+    d, buf = P.run_gpu(cfg, inp)
+    r, dec = P.check_route(cfg, host, buf, decisive_min_frac=0.5)
+    lay = P.check_layout(cfg, buf)
+    N = lay["n_kept"]
+    P.check_permute_rows(cfg, host, buf, np.arange(N))
+    P.check_ffn_rows(cfg, host, buf, np.arange(N), lay)
+    P.check_combine_tokens(cfg, buf, np.arange(cfg.T))
+    P.check_identity_experts(cfg, buf, inp["x"])

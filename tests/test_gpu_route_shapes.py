@@ -4,7 +4,7 @@ The bf16 router pads the experts to a multiple of 16 (one to sixteen 16-expert t
 tokens per block and streams 64-wide slices of D through a ring of LDS stages; these cases cover
 every padding of E, a partial last block, fewer tokens than one block, and D with fewer slices than
 the ring holds (D = 64 and 128), plus the group-limited, full-softmax and selection-bias paths on
-such shapes."""
+such shapes, and top-k up to 32."""
 import numpy as np
 import pytest
 import torch
@@ -29,6 +29,11 @@ CASES = [
      dict(gate=W.GATE_SIGMOID_TOPK, n_groups=8, topk_groups=4)),
     ("e64_t97_d128_grouped", 97, 128, 64, 4, dict(n_groups=4, topk_groups=2)),
     ("e24_t300_d64_softmax_full", 300, 64, 24, 2, dict(gate=W.GATE_SOFTMAX_FULL)),
+    # k > 16: the general one-token-per-wave selection (the 4-tokens-per-wave one takes k <= 16), up to
+    # the router's k = 32
+    ("e64_t70_d128_k20", 70, 128, 64, 20, {}),
+    ("e256_t65_d64_k32_grouped", 65, 64, 256, 32, dict(gate=W.GATE_SIGMOID_TOPK, n_groups=8, topk_groups=4)),
+    ("e40_t33_d64_k32_softmax_full", 33, 64, 40, 32, dict(gate=W.GATE_SOFTMAX_FULL)),
 ]
 
 
