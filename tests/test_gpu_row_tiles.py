@@ -5,7 +5,8 @@ counts here hit every case: an empty expert, one row, a 32-row edge, exactly one
 past it, partial second and third tiles, and an expert with more than ten tiles. Up- and down-projection (plain, gathered rows from x, and the K-major weight
 read of the backward data gradient) are compared row by row with the oracle's expert FFN on the same
 rows; the gathered up-projection equals the one on permuted rows bit for bit. A second set has more
-experts than a GEMM block has threads, which takes the tile map's multi-pass scan."""
+experts than a GEMM block has threads, which takes the tile map's multi-pass scan; and a reduction long
+enough (F = 8192) for the down-projection's earlier ring refill."""
 import numpy as np
 import pytest
 import torch
@@ -111,3 +112,31 @@ def test_more_experts_than_block_threads():
     ref = O.expert_ffn_rows(x_perm.cpu(), experts, inp["w1"].cpu(), inp["w3"].cpu(), inp["w2"].cpu(), cfg.act)
     err = rel_err_rows(f64(y), ref)
     assert err.max() <= TOL_Y[cfg.dtype], f"max rel err {err.max():.3e} at row {int(err.argmax())}"
+
+
+@needs_gpu
+def test_down_projection_with_a_long_reduction():
+    # F = 8192: the plain down-projection takes the ring that loads every other stage one k-step
+    # earlier (reductions this long); every row of ragged tiles against the oracle's expert FFN rows
+    counts = [0, 1, 33, 320, 321, 700]
+    E, N, F, D = len(counts), sum(counts), 8192, 128
+    cfg = W.MoEConfig(name="long_k", T=N, D=D, E=E, top_k=1, F=F, act=W.ACT_GELU, seed=93)
+    print(f"[row_tiles] long reduction F={F}", flush=True)
+    inp = W.make_inputs(cfg, "cuda")
+    d = M.dims_from_config(cfg)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32, device="cuda")
+    h = torch.full((N, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_up(d, inp["x"], offsets, inp["w1"], None, h)
+    y = torch.full((N, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_expert_ffn_down(d, h, offsets, inp["w2"], y)
+    torch.cuda.synchronize()
+    experts = np.repeat(np.arange(E), counts)
+    ref = O.expert_ffn_rows(inp["x"].cpu(), experts, inp["w1"].cpu(), None, inp["w2"].cpu(), W.ACT_GELU)
+    err = rel_err_rows(f64(y), ref)
+    assert err.max() <= TOL_Y[cfg.dtype], f"max rel err {err.max():.3e} at row {int(err.argmax())}"
+    # the down-projection alone on the GPU's own h, against a float64 product of the same operands
+    hh, w2 = f64(h), inp["w2"].double().cpu().numpy()
+    ref2 = np.concatenate([hh[o:o + c] @ w2[e].T for e, (o, c) in
+                           enumerate(zip(np.concatenate([[0], np.cumsum(counts)])[:-1], counts))])
+    err2 = rel_err_rows(f64(y), ref2)
+    assert err2.max() <= 8e-3, f"down-projection on the GPU's h: max rel err {err2.max():.3e}"
